@@ -1,0 +1,155 @@
+/*
+ * ar.h -- C ABI of the single-GPU AllReduce library (libar.so).
+ *
+ * N logical ranks are N equal-length buffers in one GPU's HBM.  The library
+ * reduces them elementwise (SUM, MAX, or AVG = SUM then divide by N) so that
+ * every buffer ends with the same result, the way an AllReduce leaves every
+ * participant with the reduction of all participants' data ("AllReduce",
+ * compassingai.com, section 3 技术原理; "AllReduce 集合通信", zzmblog.top,
+ * section 语义).  Operations are in place, like torch.distributed.all_reduce
+ * ("Allreduce：大模型分布式训练的核心通信算法与优化实践", pwwt.cn, section 3.2).
+ *
+ * Conventions shared by every call below:
+ *  - bufs: a HOST array of nranks DEVICE pointers, read only during the call.
+ *    The caller owns the buffers; each holds `count` elements of `dtype`,
+ *    contiguous, naturally aligned, on the context's device, and no two
+ *    buffers overlap.  1 <= nranks <= AR_MAX_RANKS.
+ *  - Chunks: element range of chunk c is given by ar_chunk_range: chunk length
+ *    L = ceil(count / nranks); chunk c = [min(c*L, count), min((c+1)*L, count)).
+ *    Trailing chunks may be short or empty when nranks does not divide count.
+ *  - Every compute call validates its arguments first and returns an error
+ *    before launching anything if they are invalid.  Otherwise it enqueues the
+ *    kernels on the context's stream and returns AR_OK without waiting; a
+ *    device fault surfaces at the caller's next synchronisation of that stream.
+ *  - count == 0 and nranks == 1 are successful no-ops (AVG over one rank is
+ *    the identity).
+ *  - No call allocates device memory: the pointer table travels by value in
+ *    the kernel arguments.
+ *  - No C++ exception crosses this interface.  A context is not thread-safe;
+ *    use one per host thread / stream.
+ *  - ar_last_error(ctx) describes the most recent failure on that context.
+ */
+#ifndef RING_ALLREDUCE_AR_H
+#define RING_ALLREDUCE_AR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_MAX_RANKS 64
+
+typedef struct ar_ctx ar_ctx;
+
+typedef enum ar_status {
+    AR_OK = 0,
+    AR_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum, overlap, step index */
+    AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, TREE on non-power-of-two N */
+    AR_ERR_RUNTIME = 3,       /* the HIP runtime reported an error */
+    AR_ERR_NO_MEMORY = 4      /* host allocation of the context failed */
+} ar_status;
+
+typedef enum ar_dtype { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BFLOAT16 = 2 } ar_dtype;
+
+/* Reduction operator.  Per-hop arithmetic: int32 SUM wraps (two's complement);
+ * fp32 SUM is one binary32 round-to-nearest-even add per hop; bf16 SUM adds in
+ * fp32 and rounds the sum to bf16 (nearest-even) at every hop; MAX is
+ * IEEE-754-2019 maximum (NaN wins, +0 > -0; a NaN result is the canonical
+ * quiet NaN).  AVG is SUM followed by one division of the finished sum by N
+ * (DDP's divide by world size: pwwt.cn page, sections 3.1-3.2): fp32 correctly
+ * rounded, bf16 rounded from the fp32 quotient.  AVG on int32 is
+ * AR_ERR_UNSUPPORTED. */
+typedef enum ar_op { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
+
+/* Algorithm.
+ *  RING_STEP  -- the ring as the pages lay it out: N-1 ReduceScatter steps then
+ *                N-1 AllGather steps, one kernel launch per step ("AllReduce",
+ *                compassingai.com, section 3; pwwt.cn page, section 2.2).
+ *                Chunk c is folded over ranks c+1, c+2, ..., c in that order.
+ *  RING_FUSED -- one kernel that reads each element from all N ranks, folds in
+ *                the same ring order with the same per-hop rounding, and writes
+ *                all N outputs: bitwise equal to RING_STEP, with the minimum
+ *                HBM traffic (N*K read + N*K written, K = bytes per rank).
+ *  TREE       -- recursive doubling ("集合通信基础AllReduce、Ring算法与NCCL全解析",
+ *                xdnf.cn, section 4.1): log2 N steps, partner r XOR 2^s, whole
+ *                vectors.  Pairwise fold order.  Power-of-two N only; AllReduce
+ *                only. */
+typedef enum ar_algo {
+    AR_ALGO_RING_STEP = 0,
+    AR_ALGO_RING_FUSED = 1,
+    AR_ALGO_TREE = 2
+} ar_algo;
+
+/* Create a context bound to HIP device `device` and stream `stream`
+ * (a hipStream_t; NULL = the device's null stream).  *out receives the
+ * context, owned by the library until ar_destroy.  Errors: out == NULL or a
+ * bad device -> AR_ERR_INVALID_ARG; allocation failure -> AR_ERR_NO_MEMORY. */
+ar_status ar_create(ar_ctx** out, int device, void* stream);
+
+/* Rebind the context to another stream (hipStream_t, NULL = null stream) of
+ * the same device.  Subsequent calls enqueue there. */
+ar_status ar_set_stream(ar_ctx* ctx, void* stream);
+
+/* AllReduce in place: every bufs[r][0:count) ends with the reduction of all
+ * ranks' inputs.  RING_STEP and RING_FUSED give identical bits; TREE gives
+ * the pairwise-order result. */
+ar_status ar_allreduce(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                       ar_dtype dtype, ar_op op, ar_algo algo);
+
+/* ReduceScatter in place ("AllReduce 集合通信", zzmblog.top, section 语义: each
+ * process ends with one shard of the reduction).  On return bufs[r] holds the
+ * finished chunk r at its natural offset (ar_chunk_range(count, nranks, r));
+ * the other chunks of bufs[r] are unspecified.  RING_STEP or RING_FUSED. */
+ar_status ar_reduce_scatter(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                            ar_dtype dtype, ar_op op, ar_algo algo);
+
+/* AllGather in place: chunk r of bufs[r] is copied, bit for bit, into chunk r
+ * of every other buffer.  ar_reduce_scatter then ar_allgather with the same
+ * algo equals ar_allreduce bitwise.  RING_STEP or RING_FUSED. */
+ar_status ar_allgather(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                       ar_dtype dtype, ar_algo algo);
+
+/* One ReduceScatter step k (0 <= k <= nranks-2) of the ring: for every rank r,
+ * chunk c = (r-k-1) mod N of bufs[r] is folded into chunk c of bufs[(r+1)%N].
+ * With AR_AVG the last step (k = N-2) also divides the finished chunk by N.
+ * Calling k = 0..N-2 in order equals ar_reduce_scatter(RING_STEP). */
+ar_status ar_ring_rs_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                          ar_dtype dtype, ar_op op, int step);
+
+/* One AllGather step k (0 <= k <= nranks-2): for every rank r, chunk
+ * c = (r-k) mod N of bufs[r] is copied into chunk c of bufs[(r+1)%N]. */
+ar_status ar_ring_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                          ar_dtype dtype, int step);
+
+/* One recursive-doubling step s (0 <= s < log2 N): every pair (r, r XOR 2^s)
+ * replaces both vectors by their elementwise combination; with AR_AVG the
+ * last step divides by N.  Power-of-two nranks only. */
+ar_status ar_tree_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                       ar_dtype dtype, ar_op op, int step);
+
+/* Chunk c's element range (host-only; touches no GPU).  Errors: nranks out of
+ * range, chunk outside [0, nranks), NULL outputs -> AR_ERR_INVALID_ARG. */
+ar_status ar_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* len);
+
+/* Plain device-to-device copy of `bytes` bytes (16-byte aligned pointers and
+ * size), used to calibrate bandwidth and hardware byte counters against a
+ * kernel of known traffic.  Enqueued on the context's stream. */
+ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes);
+
+/* Static description of a status code (never NULL). */
+const char* ar_status_string(ar_status s);
+
+/* Detail of the last failure on ctx (empty string if none; never NULL).
+ * ar_last_error(NULL) describes the last ar_create failure of this thread. */
+const char* ar_last_error(const ar_ctx* ctx);
+
+/* Destroy a context.  ar_destroy(NULL) is a no-op returning AR_OK.  Work
+ * already enqueued is not waited for. */
+ar_status ar_destroy(ar_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ALLREDUCE_AR_H */

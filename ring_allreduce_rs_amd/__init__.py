@@ -1,0 +1,157 @@
+"""Single-GPU AllReduce of N logical ranks on MI355X -- Python binding.
+
+N "ranks" are N equal-length torch tensors in one GPU's HBM.  Every call
+marshals tensor pointers into the C ABI of libar.so (include/ar.h); the HIP
+kernels do all the work, in place, on torch's current stream.  There is no
+CPU fallback: if libar.so is missing, importing this package raises.
+
+    import ring_allreduce_rs_amd as ar
+    ar.allreduce(tensors, op="avg", algo="ring_fused")
+
+The API mirrors ``torch.distributed.all_reduce`` semantics ("Allreduce：大模型
+分布式训练的核心通信算法与优化实践", section 3.2: in place, every participant
+ends with the same reduced tensor), with the participants given as a list.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import (  # noqa: F401
+    ALGOS, AR_MAX_RANKS, DTYPES, EXPORTS, LIB_PATH, OPS, ArError, Context, chunk_range, lib,
+)
+
+__all__ = [
+    "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
+    "ring_ag_step", "tree_step", "copy_", "chunk_range", "bind", "context", "LIB_PATH",
+]
+
+_ctx: dict = {}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_name(t) -> str:
+    torch = _torch()
+    m = {torch.int32: "int32", torch.float32: "float32", torch.bfloat16: "bfloat16"}
+    if t.dtype not in m:
+        raise ValueError(f"unsupported dtype {t.dtype}; use int32, float32 or bfloat16")
+    return m[t.dtype]
+
+
+def _check(tensors):
+    """Same checks the pages ask of all_reduce inputs: on the GPU, contiguous,
+    same shape and dtype on every participant (pwwt.cn page, sections 3.3
+    and 5.3)."""
+    ts = list(tensors)
+    if not 1 <= len(ts) <= AR_MAX_RANKS:
+        raise ValueError(f"need 1..{AR_MAX_RANKS} rank tensors, got {len(ts)}")
+    t0 = ts[0]
+    dt = _dtype_name(t0)
+    for i, t in enumerate(ts):
+        if not t.is_cuda:
+            raise ValueError(f"tensor {i} is not on a GPU")
+        if t.device != t0.device:
+            raise ValueError(f"tensor {i} is on {t.device}, tensor 0 on {t0.device}")
+        if t.dtype != t0.dtype:
+            raise ValueError(f"tensor {i} has dtype {t.dtype}, tensor 0 {t0.dtype}")
+        if t.numel() != t0.numel():
+            raise ValueError(f"tensor {i} has {t.numel()} elements, tensor 0 {t0.numel()}")
+        if not t.is_contiguous():
+            raise ValueError(f"tensor {i} is not contiguous")
+    return ts, dt, t0.numel(), t0.device.index or 0
+
+
+def context(device: int = 0) -> Context:
+    """The per-device context, rebound to torch's current stream."""
+    torch = _torch()
+    c = _ctx.get(device)
+    if c is None:
+        c = Context(device, torch.cuda.current_stream(device).cuda_stream)
+        _ctx[device] = c
+    c.set_stream(torch.cuda.current_stream(device).cuda_stream)
+    return c
+
+
+def allreduce(tensors, op: str = "sum", algo: str = "ring_fused"):
+    """In-place AllReduce over the rank tensors; returns them."""
+    ts, dt, count, dev = _check(tensors)
+    context(dev).allreduce_ptrs([t.data_ptr() for t in ts], count, dt, op, algo)
+    return ts
+
+
+def reduce_scatter(tensors, op: str = "sum", algo: str = "ring_fused"):
+    """In-place ReduceScatter: tensor r ends with the finished chunk r at its
+    own offset (``chunk_range``); its other chunks are unspecified."""
+    ts, dt, count, dev = _check(tensors)
+    context(dev).reduce_scatter_ptrs([t.data_ptr() for t in ts], count, dt, op, algo)
+    return ts
+
+
+def allgather(tensors, algo: str = "ring_fused"):
+    """In-place AllGather: chunk r of tensor r is copied to every tensor."""
+    ts, dt, count, dev = _check(tensors)
+    context(dev).allgather_ptrs([t.data_ptr() for t in ts], count, dt, algo)
+    return ts
+
+
+def ring_rs_step(tensors, op: str, step: int):
+    ts, dt, count, dev = _check(tensors)
+    context(dev).ring_rs_step_ptrs([t.data_ptr() for t in ts], count, dt, op, step)
+    return ts
+
+
+def ring_ag_step(tensors, step: int):
+    ts, dt, count, dev = _check(tensors)
+    context(dev).ring_ag_step_ptrs([t.data_ptr() for t in ts], count, dt, step)
+    return ts
+
+
+def tree_step(tensors, op: str, step: int):
+    ts, dt, count, dev = _check(tensors)
+    context(dev).tree_step_ptrs([t.data_ptr() for t in ts], count, dt, op, step)
+    return ts
+
+
+def copy_(dst, src):
+    """16-byte vector copy of src into dst (same byte size), on the current stream."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("copy_ needs equal byte sizes")
+    context(src.device.index or 0).copy_ptrs(dst.data_ptr(), src.data_ptr(), nbytes)
+    return dst
+
+
+class _Bound:
+    """A pre-marshalled call: the pointer array and enums are built once."""
+
+    def __init__(self, fn, args, ctx):
+        self._fn = fn
+        self._args = args
+        self._ctx = ctx
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise ArError(st, self._fn.__name__, self._ctx.last_error())
+
+
+def bind(tensors, op: str = "sum", algo: str = "ring_fused", kind: str = "allreduce"):
+    """Return a zero-argument callable that re-issues the same collective on
+    the context's current stream (for timing loops)."""
+    ts, dt, count, dev = _check(tensors)
+    ctx = context(dev)
+    arr = (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    if kind == "allreduce":
+        return _Bound(lib.ar_allreduce, (ctx.handle, arr, len(ts), count, DTYPES[dt], OPS[op],
+                                         ALGOS[algo]), ctx)
+    if kind == "reduce_scatter":
+        return _Bound(lib.ar_reduce_scatter, (ctx.handle, arr, len(ts), count, DTYPES[dt],
+                                              OPS[op], ALGOS[algo]), ctx)
+    if kind == "allgather":
+        return _Bound(lib.ar_allgather, (ctx.handle, arr, len(ts), count, DTYPES[dt],
+                                         ALGOS[algo]), ctx)
+    raise ValueError(kind)

@@ -1,0 +1,169 @@
+"""ctypes binding of libar.so -- argument marshalling only.
+
+Every reduction runs in the HIP kernels behind the C ABI (include/ar.h).  If
+the library is missing this module raises at import: there is no CPU
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libar.so")
+
+AR_MAX_RANKS = 64
+
+AR_OK = 0
+AR_ERR_INVALID_ARG = 1
+AR_ERR_UNSUPPORTED = 2
+AR_ERR_RUNTIME = 3
+AR_ERR_NO_MEMORY = 4
+
+DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
+OPS = {"sum": 0, "max": 1, "avg": 2}
+ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2}
+
+# every symbol include/ar.h declares
+EXPORTS = (
+    "ar_create", "ar_set_stream", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
+    "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_chunk_range", "ar_copy",
+    "ar_status_string", "ar_last_error", "ar_destroy",
+)
+
+
+class ArError(RuntimeError):
+    """A non-AR_OK status from the C ABI."""
+
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        self.func = func
+        self.detail = detail
+        super().__init__(f"{func}: {_status_name(status)}: {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m ring_allreduce_rs_amd._build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i, cp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_char_p
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "ar_create": ([ctypes.POINTER(vp), i, vp], i),
+        "ar_set_stream": ([vp, vp], i),
+        "ar_allreduce": ([vp, pp, i, sz, i, i, i], i),
+        "ar_reduce_scatter": ([vp, pp, i, sz, i, i, i], i),
+        "ar_allgather": ([vp, pp, i, sz, i, i], i),
+        "ar_ring_rs_step": ([vp, pp, i, sz, i, i, i], i),
+        "ar_ring_ag_step": ([vp, pp, i, sz, i, i], i),
+        "ar_tree_step": ([vp, pp, i, sz, i, i, i], i),
+        "ar_chunk_range": ([sz, i, i, ctypes.POINTER(sz), ctypes.POINTER(sz)], i),
+        "ar_copy": ([vp, vp, vp, sz], i),
+        "ar_status_string": ([i], cp),
+        "ar_last_error": ([vp], cp),
+        "ar_destroy": ([vp], i),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def _status_name(s: int) -> str:
+    return lib.ar_status_string(s).decode()
+
+
+def chunk_range(count: int, nranks: int, chunk: int) -> tuple[int, int]:
+    """(offset, length) of chunk ``chunk`` -- host-only, no GPU needed."""
+    off, ln = ctypes.c_size_t(), ctypes.c_size_t()
+    st = lib.ar_chunk_range(count, nranks, chunk, ctypes.byref(off), ctypes.byref(ln))
+    if st != AR_OK:
+        raise ArError(st, "ar_chunk_range", f"count={count} nranks={nranks} chunk={chunk}")
+    return off.value, ln.value
+
+
+class Context:
+    """An ar_ctx bound to one device and a HIP stream (a raw hipStream_t int)."""
+
+    def __init__(self, device: int = 0, stream: int | None = None):
+        h = ctypes.c_void_p()
+        st = lib.ar_create(ctypes.byref(h), device, stream or None)
+        if st != AR_OK:
+            raise ArError(st, "ar_create", lib.ar_last_error(None).decode())
+        self._h = h
+        self.device = device
+        self._stream = stream or 0
+
+    @property
+    def handle(self):
+        return self._h
+
+    def set_stream(self, stream: int | None) -> None:
+        s = stream or 0
+        if s != self._stream:
+            self._check(lib.ar_set_stream(self._h, s or None), "ar_set_stream")
+            self._stream = s
+
+    def last_error(self) -> str:
+        return lib.ar_last_error(self._h).decode()
+
+    def _check(self, st: int, func: str) -> None:
+        if st != AR_OK:
+            raise ArError(st, func, self.last_error())
+
+    # raw-pointer entry points (same names and arguments as the C ABI)
+    def allreduce_ptrs(self, ptrs, count, dtype, op, algo):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_allreduce(self._h, arr, len(ptrs), count, DTYPES[dtype], OPS[op],
+                                     ALGOS[algo]), "ar_allreduce")
+
+    def reduce_scatter_ptrs(self, ptrs, count, dtype, op, algo):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_reduce_scatter(self._h, arr, len(ptrs), count, DTYPES[dtype],
+                                          OPS[op], ALGOS[algo]), "ar_reduce_scatter")
+
+    def allgather_ptrs(self, ptrs, count, dtype, algo):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_allgather(self._h, arr, len(ptrs), count, DTYPES[dtype],
+                                     ALGOS[algo]), "ar_allgather")
+
+    def ring_rs_step_ptrs(self, ptrs, count, dtype, op, step):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_ring_rs_step(self._h, arr, len(ptrs), count, DTYPES[dtype],
+                                        OPS[op], step), "ar_ring_rs_step")
+
+    def ring_ag_step_ptrs(self, ptrs, count, dtype, step):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_ring_ag_step(self._h, arr, len(ptrs), count, DTYPES[dtype], step),
+                    "ar_ring_ag_step")
+
+    def tree_step_ptrs(self, ptrs, count, dtype, op, step):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_tree_step(self._h, arr, len(ptrs), count, DTYPES[dtype], OPS[op],
+                                     step), "ar_tree_step")
+
+    def copy_ptrs(self, dst, src, nbytes):
+        self._check(lib.ar_copy(self._h, dst, src, nbytes), "ar_copy")
+
+    def close(self) -> None:
+        if self._h:
+            lib.ar_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr_array(ptrs):
+    n = len(ptrs)
+    return (ctypes.c_void_p * max(n, 1))(*ptrs)

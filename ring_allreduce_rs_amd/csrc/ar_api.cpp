@@ -1,0 +1,435 @@
+// ar_api.cpp -- the C ABI declared in include/ar.h: argument validation,
+// chunk layout, algorithm dispatch and error reporting.  Kernels live in
+// kernels.hip; this file only decides what to launch, in which order, on the
+// context's stream.
+//
+// The ring AllReduce is ReduceScatter (N-1 steps) followed by AllGather (N-1
+// steps) ("AllReduce 集合通信", zzmblog.top, sections 语义 and 两阶段流程); the
+// tree is recursive doubling in log2 N steps ("集合通信基础AllReduce、Ring算法与
+// NCCL全解析", section 4.1).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "ar.h"
+#include "launch.h"
+
+struct ar_ctx {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    std::string last_error;
+    // the last pointer set that passed the device-memory checks
+    std::vector<uintptr_t> checked;
+    size_t checked_bytes = 0;
+};
+
+namespace {
+
+thread_local std::string g_create_error;
+
+bool debug_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("AR_DEBUG");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+ar_status fail(ar_ctx* ctx, ar_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (ctx) ctx->last_error = buf;
+    else g_create_error = buf;
+    if (debug_enabled()) std::fprintf(stderr, "[ar] error: %s\n", buf);
+    return st;
+}
+
+size_t elem_bytes(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
+
+bool valid_dtype(int d) { return d == AR_INT32 || d == AR_FLOAT32 || d == AR_BFLOAT16; }
+bool valid_op(int o) { return o == AR_SUM || o == AR_MAX || o == AR_AVG; }
+bool valid_algo(int a) {
+    return a == AR_ALGO_RING_STEP || a == AR_ALGO_RING_FUSED || a == AR_ALGO_TREE;
+}
+bool pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+
+// Makes ctx->device current for the lifetime of the guard.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        ok = prev == dev || hipSetDevice(dev) == hipSuccess;
+        if (!ok) (void)hipGetLastError();
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (ok && hipGetDevice(&cur) == hipSuccess && cur != prev && prev >= 0)
+            (void)hipSetDevice(prev);
+    }
+};
+
+// Validates everything that can be checked without touching the data.  On
+// success *vec and *mis describe the common 16-byte alignment of the buffers.
+ar_status check_buffers(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, int dtype,
+                        bool* vec, unsigned* mis) {
+    if (!bufs) return fail(ctx, AR_ERR_INVALID_ARG, "bufs is NULL");
+    if (nranks < 1 || nranks > AR_MAX_RANKS)
+        return fail(ctx, AR_ERR_INVALID_ARG, "nranks %d outside [1, %d]", nranks, AR_MAX_RANKS);
+    if (!valid_dtype(dtype)) return fail(ctx, AR_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    const size_t eb = elem_bytes((ar_dtype)dtype);
+    if (count > SIZE_MAX / eb / 2)
+        return fail(ctx, AR_ERR_INVALID_ARG, "count %zu overflows the byte size", count);
+    *vec = true;
+    *mis = 0;
+    if (count == 0) return AR_OK;
+    const size_t bytes = count * eb;
+    std::vector<std::pair<uintptr_t, int>> spans;
+    spans.reserve((size_t)nranks);
+    for (int r = 0; r < nranks; ++r) {
+        const uintptr_t p = reinterpret_cast<uintptr_t>(bufs[r]);
+        if (!p) return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] is NULL", r);
+        if (p % eb) return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] is not %zu-byte aligned", r, eb);
+        if (p > UINTPTR_MAX - bytes)
+            return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] + size wraps the address space", r);
+        spans.emplace_back(p, r);
+    }
+    std::sort(spans.begin(), spans.end());
+    for (size_t i = 1; i < spans.size(); ++i) {
+        if (spans[i - 1].first + bytes > spans[i].first)
+            return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] and bufs[%d] overlap",
+                        spans[i - 1].second, spans[i].second);
+    }
+    const unsigned m0 = (unsigned)(reinterpret_cast<uintptr_t>(bufs[0]) & 15u);
+    for (int r = 1; r < nranks; ++r)
+        if ((unsigned)(reinterpret_cast<uintptr_t>(bufs[r]) & 15u) != m0) *vec = false;
+    *mis = *vec ? m0 : 0;
+
+    // Device-memory checks: every buffer must be device memory of ctx->device
+    // and lie inside its allocation.  The last passing set is cached.
+    bool same = ctx->checked.size() == (size_t)nranks && bytes <= ctx->checked_bytes;
+    for (int r = 0; same && r < nranks; ++r)
+        same = ctx->checked[(size_t)r] == reinterpret_cast<uintptr_t>(bufs[r]);
+    if (same) return AR_OK;
+    for (int r = 0; r < nranks; ++r) {
+        hipPointerAttribute_t at;
+        std::memset(&at, 0, sizeof at);
+        if (hipPointerGetAttributes(&at, bufs[r]) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] is not a device pointer", r);
+        }
+        if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged)
+            return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] is not device memory (type %d)", r,
+                        (int)at.type);
+        if (at.device != ctx->device)
+            return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] lives on device %d, context on %d", r,
+                        at.device, ctx->device);
+        // fail closed: a buffer whose extent cannot be established is refused
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        if (hipMemGetAddressRange(&base, &size, bufs[r]) != hipSuccess || !base) {
+            (void)hipGetLastError();
+            return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d]: cannot determine its allocation", r);
+        }
+        const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+        const uintptr_t p = reinterpret_cast<uintptr_t>(bufs[r]);
+        if (p < b || p + bytes > b + size)
+            return fail(ctx, AR_ERR_INVALID_ARG,
+                        "bufs[%d]: %zu bytes run past the end of its allocation", r, bytes);
+    }
+    ctx->checked.assign((size_t)nranks, 0);
+    for (int r = 0; r < nranks; ++r) ctx->checked[(size_t)r] = reinterpret_cast<uintptr_t>(bufs[r]);
+    ctx->checked_bytes = bytes;
+    return AR_OK;
+}
+
+ar_status run(ar_ctx* ctx, const arlib::Plan& p, const arlib::RankTable& t) {
+    if (debug_enabled()) {
+        arlib::Shape sh{};
+        arlib::plan_shape(p, &sh);
+        std::fprintf(stderr,
+                     "[ar] kind=%d dtype=%d op=%d n=%d count=%zu step=%d vec=%d mis=%u "
+                     "grid=%u tiles=%u threads=%u\n",
+                     (int)p.kind, (int)p.dtype, (int)p.op, p.nranks, p.count, p.step, (int)p.vec,
+                     p.mis, sh.blocks, sh.tiles, sh.threads);
+    }
+    const hipError_t e = arlib::launch(p, t, ctx->stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return AR_OK;
+}
+
+arlib::RankTable table_of(void* const* bufs, int nranks) {
+    arlib::RankTable t;
+    std::memset(&t, 0, sizeof t);
+    for (int r = 0; r < nranks; ++r) t.p[r] = bufs[r];
+    return t;
+}
+
+arlib::Plan make_plan(arlib::Kind k, int dtype, int op, int nranks, size_t count, int step,
+                      bool vec, unsigned mis) {
+    arlib::Plan p;
+    p.kind = k;
+    p.dtype = (ar_dtype)dtype;
+    p.op = (ar_op)op;
+    p.nranks = nranks;
+    p.count = count;
+    p.step = step;
+    p.vec = vec;
+    p.mis = mis;
+    return p;
+}
+
+ar_status check_op(ar_ctx* ctx, int dtype, int op) {
+    if (!valid_op(op)) return fail(ctx, AR_ERR_INVALID_ARG, "unknown op %d", op);
+    if (op == AR_AVG && dtype == AR_INT32)
+        return fail(ctx, AR_ERR_UNSUPPORTED, "AVG is defined for float32 and bfloat16 only");
+    return AR_OK;
+}
+
+ar_status check_shape(ar_ctx* ctx, arlib::Kind k, int dtype, int nranks, size_t count,
+                      bool vec) {
+    arlib::Plan p = make_plan(k, dtype, AR_SUM, nranks, count, 0, vec, 0);
+    arlib::Shape sh;
+    if (!arlib::plan_shape(p, &sh))
+        return fail(ctx, AR_ERR_INVALID_ARG, "count %zu needs more blocks than one grid holds",
+                    count);
+    return AR_OK;
+}
+
+// The collective entry points share this body.
+enum Coll { COLL_AR, COLL_RS, COLL_AG };
+
+ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size_t count,
+                     int dtype, int op, int algo) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    try {
+        if (!valid_algo(algo)) return fail(ctx, AR_ERR_INVALID_ARG, "unknown algo %d", algo);
+        if (coll != COLL_AG) {
+            const ar_status s = check_op(ctx, dtype, op);
+            if (s != AR_OK && valid_dtype(dtype)) return s;
+        }
+        bool vec = true;
+        unsigned mis = 0;
+        ar_status s = check_buffers(ctx, bufs, nranks, count, dtype, &vec, &mis);
+        if (s != AR_OK) return s;
+        if (algo == AR_ALGO_TREE) {
+            if (coll != COLL_AR)
+                return fail(ctx, AR_ERR_UNSUPPORTED,
+                            "TREE is an AllReduce algorithm; use RING_STEP or RING_FUSED");
+            if (!pow2(nranks))
+                return fail(ctx, AR_ERR_UNSUPPORTED,
+                            "TREE (recursive doubling) needs a power-of-two nranks, got %d",
+                            nranks);
+        }
+        if (count == 0 || nranks == 1) return AR_OK;
+        const arlib::Kind probe = algo == AR_ALGO_TREE ? arlib::KIND_TREE_STEP : arlib::KIND_RS_STEP;
+        s = check_shape(ctx, probe, dtype, nranks, count, vec);
+        if (s != AR_OK) return s;
+
+        DeviceGuard g(ctx->device);
+        if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
+        const arlib::RankTable t = table_of(bufs, nranks);
+        const int o = coll == COLL_AG ? AR_SUM : op;
+        if (algo == AR_ALGO_RING_FUSED) {
+            const arlib::Kind k = coll == COLL_AR   ? arlib::KIND_FUSED_AR
+                                  : coll == COLL_RS ? arlib::KIND_FUSED_RS
+                                                    : arlib::KIND_FUSED_AG;
+            return run(ctx, make_plan(k, dtype, o, nranks, count, 0, vec, mis), t);
+        }
+        if (algo == AR_ALGO_TREE) {
+            for (int st = 0; (1 << st) < nranks; ++st) {
+                s = run(ctx, make_plan(arlib::KIND_TREE_STEP, dtype, o, nranks, count, st, vec, mis),
+                        t);
+                if (s != AR_OK) return s;
+            }
+            return AR_OK;
+        }
+        if (coll != COLL_AG) {
+            for (int k = 0; k <= nranks - 2; ++k) {
+                s = run(ctx, make_plan(arlib::KIND_RS_STEP, dtype, o, nranks, count, k, vec, mis), t);
+                if (s != AR_OK) return s;
+            }
+        }
+        if (coll != COLL_RS) {
+            for (int k = 0; k <= nranks - 2; ++k) {
+                s = run(ctx, make_plan(arlib::KIND_AG_STEP, dtype, o, nranks, count, k, vec, mis), t);
+                if (s != AR_OK) return s;
+            }
+        }
+        return AR_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(ctx, AR_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
+    }
+}
+
+ar_status single_step(ar_ctx* ctx, arlib::Kind kind, void* const* bufs, int nranks, size_t count,
+                      int dtype, int op, int step) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    try {
+        if (kind != arlib::KIND_AG_STEP) {
+            const ar_status s = check_op(ctx, dtype, op);
+            if (s != AR_OK && valid_dtype(dtype)) return s;
+        }
+        bool vec = true;
+        unsigned mis = 0;
+        ar_status s = check_buffers(ctx, bufs, nranks, count, dtype, &vec, &mis);
+        if (s != AR_OK) return s;
+        int nsteps = nranks - 1;
+        if (kind == arlib::KIND_TREE_STEP) {
+            if (!pow2(nranks))
+                return fail(ctx, AR_ERR_UNSUPPORTED,
+                            "TREE (recursive doubling) needs a power-of-two nranks, got %d",
+                            nranks);
+            nsteps = 0;
+            while ((1 << nsteps) < nranks) ++nsteps;
+        }
+        if (step < 0 || step >= nsteps)
+            return fail(ctx, AR_ERR_INVALID_ARG, "step %d outside [0, %d)", step, nsteps);
+        if (count == 0) return AR_OK;
+        s = check_shape(ctx, kind, dtype, nranks, count, vec);
+        if (s != AR_OK) return s;
+        DeviceGuard g(ctx->device);
+        if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
+        const int o = kind == arlib::KIND_AG_STEP ? AR_SUM : op;
+        return run(ctx, make_plan(kind, dtype, o, nranks, count, step, vec, mis),
+                   table_of(bufs, nranks));
+    } catch (...) {
+        return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
+    }
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+ar_status ar_create(ar_ctx** out, int device, void* stream) {
+    if (!out) return fail(nullptr, AR_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(nullptr, AR_ERR_RUNTIME, "no HIP device available");
+    }
+    if (device < 0 || device >= ndev)
+        return fail(nullptr, AR_ERR_INVALID_ARG, "device %d outside [0, %d)", device, ndev);
+    ar_ctx* c = new (std::nothrow) ar_ctx();
+    if (!c) return fail(nullptr, AR_ERR_NO_MEMORY, "cannot allocate the context");
+    c->device = device;
+    c->stream = reinterpret_cast<hipStream_t>(stream);
+    *out = c;
+    return AR_OK;
+}
+
+ar_status ar_set_stream(ar_ctx* ctx, void* stream) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->stream = reinterpret_cast<hipStream_t>(stream);
+    return AR_OK;
+}
+
+ar_status ar_allreduce(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
+                       ar_op op, ar_algo algo) {
+    return collective(ctx, COLL_AR, bufs, nranks, count, (int)dtype, (int)op, (int)algo);
+}
+
+ar_status ar_reduce_scatter(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                            ar_dtype dtype, ar_op op, ar_algo algo) {
+    return collective(ctx, COLL_RS, bufs, nranks, count, (int)dtype, (int)op, (int)algo);
+}
+
+ar_status ar_allgather(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
+                       ar_algo algo) {
+    return collective(ctx, COLL_AG, bufs, nranks, count, (int)dtype, AR_SUM, (int)algo);
+}
+
+ar_status ar_ring_rs_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                          ar_dtype dtype, ar_op op, int step) {
+    return single_step(ctx, arlib::KIND_RS_STEP, bufs, nranks, count, (int)dtype, (int)op, step);
+}
+
+ar_status ar_ring_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                          ar_dtype dtype, int step) {
+    return single_step(ctx, arlib::KIND_AG_STEP, bufs, nranks, count, (int)dtype, AR_SUM, step);
+}
+
+ar_status ar_tree_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
+                       ar_op op, int step) {
+    return single_step(ctx, arlib::KIND_TREE_STEP, bufs, nranks, count, (int)dtype, (int)op, step);
+}
+
+ar_status ar_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* len) {
+    if (!offset || !len || nranks < 1 || nranks > AR_MAX_RANKS || chunk < 0 || chunk >= nranks)
+        return AR_ERR_INVALID_ARG;
+    const size_t per = count / (size_t)nranks + (count % (size_t)nranks ? 1 : 0);
+    size_t lo = (size_t)chunk * per;
+    if (lo > count) lo = count;
+    size_t hi = lo + per;
+    if (hi > count) hi = count;
+    *offset = lo;
+    *len = hi - lo;
+    return AR_OK;
+}
+
+ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    if (bytes == 0) return AR_OK;
+    if (!dst || !src) return fail(ctx, AR_ERR_INVALID_ARG, "NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) | bytes) & 15u)
+        return fail(ctx, AR_ERR_INVALID_ARG, "ar_copy needs 16-byte aligned pointers and size");
+    void* const pair[2] = {dst, const_cast<void*>(src)};
+    bool vec;
+    unsigned mis;
+    const ar_status s = check_buffers(ctx, pair, 2, bytes / 4, AR_INT32, &vec, &mis);
+    if (s != AR_OK) return s;
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
+    const hipError_t e = arlib::launch_copy(dst, src, bytes, ctx->stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_RUNTIME, "copy launch failed: %s", hipGetErrorString(e));
+    }
+    return AR_OK;
+}
+
+const char* ar_status_string(ar_status s) {
+    switch (s) {
+        case AR_OK: return "AR_OK";
+        case AR_ERR_INVALID_ARG: return "AR_ERR_INVALID_ARG";
+        case AR_ERR_UNSUPPORTED: return "AR_ERR_UNSUPPORTED";
+        case AR_ERR_RUNTIME: return "AR_ERR_RUNTIME";
+        case AR_ERR_NO_MEMORY: return "AR_ERR_NO_MEMORY";
+    }
+    return "AR_ERR_UNKNOWN";
+}
+
+const char* ar_last_error(const ar_ctx* ctx) {
+    return ctx ? ctx->last_error.c_str() : g_create_error.c_str();
+}
+
+ar_status ar_destroy(ar_ctx* ctx) {
+    delete ctx;
+    return AR_OK;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,178 @@
+// elem.h -- device-side element arithmetic of one ring hop (gfx950).
+//
+// A hop combines the partial result travelling round the ring with the
+// receiving rank's own element.  The pages name the reduction (sum, max) and
+// the DDP average (sum, then divide by the world size: "Allreduce：大模型分布式
+// 训练的核心通信算法与优化实践", sections 3.1-3.2) but not its arithmetic; the
+// rules implemented here are:
+//   int32 SUM  two's-complement wrap-around add
+//   fp32  SUM  one binary32 add, round to nearest even (no contraction, no
+//              wider accumulator, subnormals kept)
+//   bf16  SUM  widen both to fp32, add in fp32, round the sum to bf16
+//              (nearest even) -- every hop rounds
+//   MAX        IEEE-754-2019 maximum: NaN wins (canonical quiet NaN), +0 > -0
+//   AVG        finished SUM divided once by N: fp32 correctly rounded
+//              division; bf16 rounds the fp32 quotient
+//
+// Storage is handled as raw 32-bit words so one 16-byte load feeds 4 fp32 /
+// int32 lanes or 8 bf16 lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace arlib {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float as_f32(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f); }
+
+// IEEE-754-2019 maximum of two binary32 bit patterns.  Equal values differ at
+// most in the sign of a zero; AND-ing the patterns gives -0 only if both are -0.
+__device__ __forceinline__ uint32_t fmaximum_bits(uint32_t a, uint32_t b) {
+    const float fa = as_f32(a), fb = as_f32(b);
+    if (fa != fa || fb != fb) return 0x7fc00000u;
+    if (fa == fb) return a & b;
+    return fa > fb ? a : b;
+}
+
+// binary32 -> bf16, round to nearest, ties to even, on the bit pattern:
+// adding 0x7FFF plus the lowest kept bit carries into the kept half exactly
+// when the dropped half exceeds one half, or equals it with an odd kept half.
+// NaN -> canonical quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = as_u32(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_widen(uint32_t h) { return as_f32(h << 16); }
+
+// Every op exposes: element size, one-element combine/finish on the low bits
+// of a word, and whole-word combine/finish (two bf16 per word).
+struct OpI32Sum {
+    static constexpr int kElemBytes = 4;
+    __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) { return a + b; }
+    __device__ static uint32_t finish_elem(uint32_t a, float) { return a; }
+    __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return a + b; }
+    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+};
+
+struct OpI32Max {
+    static constexpr int kElemBytes = 4;
+    __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) {
+        return (int32_t)a > (int32_t)b ? a : b;
+    }
+    __device__ static uint32_t finish_elem(uint32_t a, float) { return a; }
+    __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return comb_elem(a, b); }
+    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+};
+
+struct OpF32Sum {
+    static constexpr int kElemBytes = 4;
+    __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) {
+        return as_u32(__fadd_rn(as_f32(a), as_f32(b)));
+    }
+    __device__ static uint32_t finish_elem(uint32_t a, float nf) {
+        return as_u32(__fdiv_rn(as_f32(a), nf));
+    }
+    __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return comb_elem(a, b); }
+    __device__ static uint32_t finish_word(uint32_t a, float nf) { return finish_elem(a, nf); }
+};
+
+struct OpF32Max {
+    static constexpr int kElemBytes = 4;
+    __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) { return fmaximum_bits(a, b); }
+    __device__ static uint32_t finish_elem(uint32_t a, float) { return a; }
+    __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return fmaximum_bits(a, b); }
+    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+};
+
+struct OpBF16Sum {
+    static constexpr int kElemBytes = 2;
+    __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) {
+        return bf16_rne(__fadd_rn(bf16_widen(a & 0xffffu), bf16_widen(b & 0xffffu)));
+    }
+    __device__ static uint32_t finish_elem(uint32_t a, float nf) {
+        return bf16_rne(__fdiv_rn(bf16_widen(a & 0xffffu), nf));
+    }
+    __device__ static uint32_t comb_word(uint32_t a, uint32_t b) {
+        return comb_elem(a, b) | (comb_elem(a >> 16, b >> 16) << 16);
+    }
+    __device__ static uint32_t finish_word(uint32_t a, float nf) {
+        return finish_elem(a, nf) | (finish_elem(a >> 16, nf) << 16);
+    }
+};
+
+struct OpBF16Max {
+    static constexpr int kElemBytes = 2;
+    // the maximum of two bf16 values is one of them, so it needs no rounding
+    __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) {
+        const uint32_t m = fmaximum_bits((a & 0xffffu) << 16, (b & 0xffffu) << 16);
+        return m >> 16;
+    }
+    __device__ static uint32_t finish_elem(uint32_t a, float) { return a & 0xffffu; }
+    __device__ static uint32_t comb_word(uint32_t a, uint32_t b) {
+        return comb_elem(a, b) | (comb_elem(a >> 16, b >> 16) << 16);
+    }
+    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+};
+
+// Copy-only "op" for the AllGather paths (element size matters, values do not).
+template <int EB>
+struct OpCopy {
+    static constexpr int kElemBytes = EB;
+};
+
+// ---------------------------------------------------------------- memory units
+//
+// A Unit is what one lane moves per access: 16 bytes on the vector path, one
+// element on the scalar path (used for the unaligned head and tail of a chunk,
+// and for buffers whose addresses disagree modulo 16).
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+template <int EB>
+__device__ __forceinline__ uint32_t ld_elem(const void* p) {
+    if constexpr (EB == 4) return *reinterpret_cast<const uint32_t*>(p);
+    else return *reinterpret_cast<const uint16_t*>(p);
+}
+
+template <int EB>
+__device__ __forceinline__ void st_elem(void* p, uint32_t v) {
+    if constexpr (EB == 4) *reinterpret_cast<uint32_t*>(p) = v;
+    else *reinterpret_cast<uint16_t*>(p) = (uint16_t)v;
+}
+
+template <class Op>
+__device__ __forceinline__ u32x4 comb4(u32x4 a, u32x4 b) {
+    u32x4 r;
+    r.x = Op::comb_word(a.x, b.x);
+    r.y = Op::comb_word(a.y, b.y);
+    r.z = Op::comb_word(a.z, b.z);
+    r.w = Op::comb_word(a.w, b.w);
+    return r;
+}
+
+template <class Op>
+__device__ __forceinline__ u32x4 finish4(u32x4 a, float nf) {
+    u32x4 r;
+    r.x = Op::finish_word(a.x, nf);
+    r.y = Op::finish_word(a.y, nf);
+    r.z = Op::finish_word(a.z, nf);
+    r.w = Op::finish_word(a.w, nf);
+    return r;
+}
+
+}  // namespace arlib

@@ -1,0 +1,469 @@
+// kernels.hip -- HIP kernels of the ring / tree AllReduce for CDNA4 (gfx950).
+//
+// All N logical ranks are buffers in one GPU's HBM.  The path is pure
+// streaming (about (N-1)/(8N) flop per byte for fp32), so every kernel is
+// built around 16-byte coalesced loads and stores: consecutive lanes of a
+// 64-wide wavefront touch consecutive 16 bytes of the same rank buffer.  No
+// LDS, no MFMA -- nothing here is a contraction.
+//
+// Ring schedule (pwwt.cn page "Allreduce：大模型分布式训练的核心通信算法与优化实践",
+// section 2.2, read as: ReduceScatter step k sends chunk (r-k-1) mod N from
+// rank r to rank r+1; AllGather step k forwards chunk (r-k) mod N).  Chunk c
+// is therefore folded over ranks c+1, c+2, ..., c-1, c, left to right, and
+// ends on rank c.
+//
+// Kernels:
+//   k_fused<MODE>  one pass; each lane loads one 16-byte unit from every rank
+//                  (in ring order, kBatch ranks of loads in flight before the
+//                  adds), folds them in order in registers, and stores the
+//                  result to all N ranks (AllReduce), to the owner only
+//                  (ReduceScatter) or copies the owner's unit to the others
+//                  (AllGather).  Bitwise equal to the per-step ring because the
+//                  fold order and per-hop rounding are the same.
+//   k_rs_step      one ReduceScatter step: every rank's chunk folded into its
+//                  successor's copy (AVG divide fused into the last step).
+//   k_ag_step      one AllGather step: chunk copied to the successor.
+//   k_tree_step    one recursive-doubling step ("集合通信基础AllReduce、Ring算法
+//                  与NCCL全解析", section 4.1): both partners of a pair get the
+//                  combination of their vectors.
+//   k_copy         plain 16-byte copy, the bandwidth / counter calibration.
+//
+// Block -> work mapping: block b handles tile (b mod tiles) of chunk
+// (b / tiles), so the chunk -- and with it the first rank of the fold and
+// every rank pointer -- is uniform across the block and lives in scalar
+// registers.  A chunk whose start is not 16-byte aligned (counts not divisible
+// by N, e.g. 268,435,459 over 16 ranks) has a head of up to 15 bytes and a
+// tail, handled element by element by lanes of the chunk's first tile.
+#include "elem.h"
+#include "launch.h"
+
+namespace arlib {
+
+constexpr int kThreads = 256;  // 4 wavefronts of 64
+constexpr int kUnroll = 2;     // 16-byte units per lane per tile
+constexpr int kBatch = 8;      // ranks of loads issued before they are folded
+constexpr bool kNonTemporal = false;
+
+struct Args {
+    RankTable t;
+    size_t count;     // elements per rank
+    size_t per;       // chunk length L = ceil(count / N)
+    int n;            // ranks
+    int step;         // step index (per-step kernels)
+    unsigned tiles;   // tiles per chunk (per pair for the tree)
+    unsigned mis;     // every buffer's address mod 16, in bytes
+    int avg;          // 1: divide the finished sum by n
+    float nf;         // (float)n
+};
+
+template <class Op, bool VEC>
+struct Unit;
+
+template <class Op>
+struct Unit<Op, true> {
+    using T = u32x4;
+    static constexpr int kBytes = 16;
+    __device__ static T ld(const char* p) { return ld16<kNonTemporal>(p); }
+    __device__ static void st(char* p, T v) { st16<kNonTemporal>(p, v); }
+    __device__ static T comb(T a, T b) { return comb4<Op>(a, b); }
+    __device__ static T fin(T a, float nf) { return finish4<Op>(a, nf); }
+    __device__ static T zero() { return u32x4{0u, 0u, 0u, 0u}; }
+};
+
+template <class Op>
+struct Unit<Op, false> {
+    using T = uint32_t;
+    static constexpr int kBytes = Op::kElemBytes;
+    __device__ static T ld(const char* p) { return ld_elem<Op::kElemBytes>(p); }
+    __device__ static void st(char* p, T v) { st_elem<Op::kElemBytes>(p, v); }
+    __device__ static T comb(T a, T b) { return Op::comb_elem(a, b); }
+    __device__ static T fin(T a, float nf) { return Op::finish_elem(a, nf); }
+    __device__ static T zero() { return 0u; }
+};
+
+// Split the element range [lo, lo+len) into an element-wise head up to the
+// first 16-byte boundary, a body of 16-byte units, and an element-wise tail.
+struct Span {
+    size_t body;     // first element of the body
+    size_t units;    // body length in units
+    size_t tail;     // first tail element
+    unsigned nhead;  // head elements, starting at lo
+    unsigned ntail;  // tail elements
+};
+
+template <int EB, bool VEC>
+__device__ __forceinline__ Span make_span(size_t lo, size_t len, unsigned mis) {
+    Span s;
+    if constexpr (VEC) {
+        constexpr int kEpu = 16 / EB;
+        const unsigned m = (unsigned)((mis + lo * EB) & 15u);
+        size_t h = m ? (16u - m) / EB : 0;
+        if (h > len) h = len;
+        s.nhead = (unsigned)h;
+        s.body = lo + h;
+        s.units = (len - h) / kEpu;
+        s.tail = s.body + s.units * kEpu;
+        s.ntail = (unsigned)(lo + len - s.tail);
+    } else {
+        s.nhead = 0;
+        s.body = lo;
+        s.units = len;
+        s.tail = lo + len;
+        s.ntail = 0;
+    }
+    return s;
+}
+
+__device__ __forceinline__ void chunk_bounds(const Args& a, int c, size_t& lo, size_t& len) {
+    size_t b0 = (size_t)c * a.per;
+    if (b0 > a.count) b0 = a.count;
+    size_t b1 = b0 + a.per;
+    if (b1 > a.count) b1 = a.count;
+    lo = b0;
+    len = b1 - b0;
+}
+
+__device__ __forceinline__ char* rank_ptr(const Args& a, int r) {
+    return reinterpret_cast<char*>(a.t.p[r]);
+}
+
+// ---------------------------------------------------------------- fused ring
+
+// Units ubase, ubase+kThreads, ... (kUnroll of them, bounded by `units`) of
+// the range starting at byte offset byte0 in every rank buffer.
+template <class Op, int MODE, bool VEC>
+__device__ __forceinline__ void fused_units(const Args& a, int c, int start, size_t byte0,
+                                            size_t ubase, size_t units) {
+    using X = Unit<Op, VEC>;
+    using T = typename X::T;
+    const int n = a.n;
+    bool ok[kUnroll];
+    size_t off[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t idx = ubase + (size_t)u * kThreads;
+        ok[u] = idx < units;
+        off[u] = byte0 + idx * X::kBytes;
+    }
+    T acc[kUnroll];
+    if constexpr (MODE == KIND_FUSED_AG) {
+        const char* src = rank_ptr(a, c);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc[u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+        for (int r = 0; r < n; ++r) {
+            if (r == c) continue;
+            char* dst = rank_ptr(a, r);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if (ok[u]) X::st(dst + off[u], acc[u]);
+        }
+        return;
+    } else {
+        // ring order: start = c+1, then c+2, ..., ending with c itself
+        int r = start;
+        for (int j0 = 0; j0 < n; j0 += kBatch) {
+            T v[kBatch][kUnroll];
+            int rr = r;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (j0 + j < n) {
+                    const char* src = rank_ptr(a, rr);
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u)
+                        v[j][u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+                    rr = (rr + 1 == n) ? 0 : rr + 1;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (j0 + j < n) {
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u)
+                        acc[u] = (j0 + j == 0) ? v[j][u] : X::comb(acc[u], v[j][u]);
+                }
+            }
+            r = rr;
+        }
+        if (a.avg) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) acc[u] = X::fin(acc[u], a.nf);
+        }
+        if constexpr (MODE == KIND_FUSED_RS) {
+            char* dst = rank_ptr(a, c);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if (ok[u]) X::st(dst + off[u], acc[u]);
+        } else {
+            for (int r2 = 0; r2 < n; ++r2) {
+                char* dst = rank_ptr(a, r2);
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (ok[u]) X::st(dst + off[u], acc[u]);
+            }
+        }
+    }
+}
+
+template <class Op, int MODE, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_fused(const Args a) {
+    constexpr int EB = Op::kElemBytes;
+    const int n = a.n;
+    const int c = (int)(blockIdx.x / a.tiles);
+    const unsigned tile = blockIdx.x - (unsigned)c * a.tiles;
+    size_t lo, len;
+    chunk_bounds(a, c, lo, len);
+    if (len == 0) return;
+    const Span sp = make_span<EB, VEC>(lo, len, a.mis);
+    const int start = (c + 1 == n) ? 0 : c + 1;
+    const size_t ubase = (size_t)tile * (kThreads * kUnroll) + threadIdx.x;
+    if (ubase < sp.units)
+        fused_units<Op, MODE, VEC>(a, c, start, sp.body * EB, ubase, sp.units);
+    if constexpr (VEC) {
+        if (tile == 0) {
+            const unsigned t = threadIdx.x;
+            if (t < sp.nhead)
+                fused_units<Op, MODE, false>(a, c, start, (lo + t) * EB, 0, 1);
+            else if (t >= 64 && t - 64 < sp.ntail)
+                fused_units<Op, MODE, false>(a, c, start, (sp.tail + (t - 64)) * EB, 0, 1);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- per-step ring and tree
+
+// dst[i] <- comb(src[i], dst[i]) (REDUCE) or dst[i] <- src[i] (copy); with
+// `both`, src[i] also receives the combination (tree).
+template <class Op, bool VEC, bool REDUCE, bool BOTH>
+__device__ __forceinline__ void pair_units(char* src, char* dst, size_t byte0, size_t ubase,
+                                           size_t units, bool fin, float nf) {
+    using X = Unit<Op, VEC>;
+    using T = typename X::T;
+    bool ok[kUnroll];
+    size_t off[kUnroll];
+    T x[kUnroll], y[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t idx = ubase + (size_t)u * kThreads;
+        ok[u] = idx < units;
+        off[u] = byte0 + idx * X::kBytes;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        x[u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+        if constexpr (REDUCE) y[u] = ok[u] ? X::ld(dst + off[u]) : X::zero();
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        T z = x[u];
+        if constexpr (REDUCE) {
+            z = X::comb(x[u], y[u]);
+            if (fin) z = X::fin(z, nf);
+        }
+        if (ok[u]) {
+            X::st(dst + off[u], z);
+            if constexpr (BOTH) X::st(src + off[u], z);
+        }
+    }
+}
+
+template <class Op, bool VEC, bool REDUCE, bool BOTH>
+__device__ __forceinline__ void pair_range(char* src, char* dst, size_t lo, size_t len,
+                                           unsigned mis, unsigned tile, bool fin, float nf) {
+    constexpr int EB = Op::kElemBytes;
+    const Span sp = make_span<EB, VEC>(lo, len, mis);
+    const size_t ubase = (size_t)tile * (kThreads * kUnroll) + threadIdx.x;
+    if (ubase < sp.units)
+        pair_units<Op, VEC, REDUCE, BOTH>(src, dst, sp.body * EB, ubase, sp.units, fin, nf);
+    if constexpr (VEC) {
+        if (tile == 0) {
+            const unsigned t = threadIdx.x;
+            if (t < sp.nhead)
+                pair_units<Op, false, REDUCE, BOTH>(src, dst, (lo + t) * EB, 0, 1, fin, nf);
+            else if (t >= 64 && t - 64 < sp.ntail)
+                pair_units<Op, false, REDUCE, BOTH>(src, dst, (sp.tail + (t - 64)) * EB, 0, 1,
+                                                    fin, nf);
+        }
+    }
+}
+
+// ReduceScatter step k: rank r folds its chunk (r-k-1) mod N into rank r+1.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_rs_step(const Args a) {
+    const int n = a.n;
+    const int r = (int)(blockIdx.x / a.tiles);
+    const unsigned tile = blockIdx.x - (unsigned)r * a.tiles;
+    const int c = (r + 2 * n - a.step - 1) % n;
+    const int d = (r + 1 == n) ? 0 : r + 1;
+    size_t lo, len;
+    chunk_bounds(a, c, lo, len);
+    if (len == 0) return;
+    const bool fin = a.avg && a.step == n - 2;   // the receiver now owns chunk c
+    pair_range<Op, VEC, true, false>(rank_ptr(a, r), rank_ptr(a, d), lo, len, a.mis, tile,
+                                     fin, a.nf);
+}
+
+// AllGather step k: rank r forwards chunk (r-k) mod N to rank r+1 unchanged.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_ag_step(const Args a) {
+    const int n = a.n;
+    const int r = (int)(blockIdx.x / a.tiles);
+    const unsigned tile = blockIdx.x - (unsigned)r * a.tiles;
+    const int c = (r + n - a.step) % n;
+    const int d = (r + 1 == n) ? 0 : r + 1;
+    size_t lo, len;
+    chunk_bounds(a, c, lo, len);
+    if (len == 0) return;
+    pair_range<Op, VEC, false, false>(rank_ptr(a, r), rank_ptr(a, d), lo, len, a.mis, tile,
+                                      false, a.nf);
+}
+
+// Recursive-doubling step s: pair q is (r, r | 2^s) with bit s of r clear.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_tree_step(const Args a) {
+    const unsigned q = blockIdx.x / a.tiles;
+    const unsigned tile = blockIdx.x - q * a.tiles;
+    const int s = a.step;
+    const unsigned low = q & ((1u << s) - 1u);
+    const int r = (int)(((q >> s) << (s + 1)) | low);
+    const int p = r | (1 << s);
+    const bool fin = a.avg && (2 << s) == a.n;   // last step
+    pair_range<Op, VEC, true, true>(rank_ptr(a, p), rank_ptr(a, r), 0, a.count, a.mis, tile,
+                                    fin, a.nf);
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy(u32x4* __restrict__ dst,
+                                                   const u32x4* __restrict__ src, size_t nvec) {
+    const size_t base = (size_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t i = base + (size_t)u * kThreads;
+        v[u] = i < nvec ? ld16<kNonTemporal>(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t i = base + (size_t)u * kThreads;
+        if (i < nvec) st16<kNonTemporal>(dst + i, v[u]);
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+static int elem_bytes(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
+
+static size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
+
+bool plan_shape(const Plan& p, Shape* out) {
+    const size_t eb = (size_t)elem_bytes(p.dtype);
+    const size_t epu = p.vec ? 16 / eb : 1;
+    const size_t per_tile = (size_t)kThreads * kUnroll;
+    size_t tiles, groups;
+    if (p.kind == KIND_TREE_STEP) {
+        tiles = ceil_div(ceil_div(p.count, epu), per_tile);
+        groups = (size_t)p.nranks / 2;
+    } else {
+        const size_t per = ceil_div(p.count, (size_t)p.nranks);
+        tiles = ceil_div(ceil_div(per, epu), per_tile);
+        groups = (size_t)p.nranks;
+    }
+    if (tiles == 0) tiles = 1;
+    const size_t blocks = tiles * groups;
+    if (blocks == 0 || blocks > 0x7fffffffu || tiles > 0xffffffffu) return false;
+    out->blocks = (unsigned)blocks;
+    out->threads = kThreads;
+    out->tiles = (unsigned)tiles;
+    return true;
+}
+
+template <class Op, bool VEC>
+static hipError_t launch_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    const dim3 block(kThreads);
+    switch (p.kind) {
+        case KIND_FUSED_AR:
+            hipLaunchKernelGGL((k_fused<Op, KIND_FUSED_AR, VEC>), grid, block, 0, s, a);
+            break;
+        case KIND_FUSED_RS:
+            hipLaunchKernelGGL((k_fused<Op, KIND_FUSED_RS, VEC>), grid, block, 0, s, a);
+            break;
+        case KIND_RS_STEP:
+            hipLaunchKernelGGL((k_rs_step<Op, VEC>), grid, block, 0, s, a);
+            break;
+        case KIND_TREE_STEP:
+            hipLaunchKernelGGL((k_tree_step<Op, VEC>), grid, block, 0, s, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int EB, bool VEC>
+static hipError_t launch_copy_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    const dim3 block(kThreads);
+    using Op = OpCopy<EB>;
+    switch (p.kind) {
+        case KIND_FUSED_AG:
+            hipLaunchKernelGGL((k_fused<Op, KIND_FUSED_AG, VEC>), grid, block, 0, s, a);
+            break;
+        case KIND_AG_STEP:
+            hipLaunchKernelGGL((k_ag_step<Op, VEC>), grid, block, 0, s, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <class Op>
+static hipError_t launch_op(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    return p.vec ? launch_kind<Op, true>(p, a, grid, s) : launch_kind<Op, false>(p, a, grid, s);
+}
+
+hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream) {
+    Shape sh;
+    if (!plan_shape(p, &sh)) return hipErrorInvalidConfiguration;
+    Args a;
+    a.t = t;
+    a.count = p.count;
+    a.per = ceil_div(p.count, (size_t)p.nranks);
+    a.n = p.nranks;
+    a.step = p.step;
+    a.tiles = sh.tiles;
+    a.mis = p.mis;
+    a.avg = p.op == AR_AVG ? 1 : 0;
+    a.nf = (float)p.nranks;
+    const dim3 grid(sh.blocks);
+
+    if (p.kind == KIND_FUSED_AG || p.kind == KIND_AG_STEP) {
+        if (elem_bytes(p.dtype) == 2)
+            return p.vec ? launch_copy_kind<2, true>(p, a, grid, stream)
+                         : launch_copy_kind<2, false>(p, a, grid, stream);
+        return p.vec ? launch_copy_kind<4, true>(p, a, grid, stream)
+                     : launch_copy_kind<4, false>(p, a, grid, stream);
+    }
+    const bool mx = p.op == AR_MAX;
+    switch (p.dtype) {
+        case AR_INT32:
+            return mx ? launch_op<OpI32Max>(p, a, grid, stream)
+                      : launch_op<OpI32Sum>(p, a, grid, stream);
+        case AR_FLOAT32:
+            return mx ? launch_op<OpF32Max>(p, a, grid, stream)
+                      : launch_op<OpF32Sum>(p, a, grid, stream);
+        case AR_BFLOAT16:
+            return mx ? launch_op<OpBF16Max>(p, a, grid, stream)
+                      : launch_op<OpBF16Sum>(p, a, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    const size_t nvec = bytes / 16;
+    if (nvec == 0) return hipSuccess;
+    const size_t blocks = ceil_div(nvec, (size_t)kThreads * kUnroll);
+    if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), nvec);
+    return hipGetLastError();
+}
+
+}  // namespace arlib

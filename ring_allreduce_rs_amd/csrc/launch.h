@@ -1,0 +1,53 @@
+// launch.h -- internal interface between the C-ABI host layer (ar_api.cpp)
+// and the HIP kernels (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ar.h"
+
+namespace arlib {
+
+// The N rank pointers travel by value in the kernel arguments.
+struct RankTable {
+    void* p[AR_MAX_RANKS];
+};
+
+enum Kind {
+    KIND_FUSED_AR = 0,   // fold every chunk in ring order, write all N ranks
+    KIND_FUSED_RS = 1,   // fold chunk r in ring order, write rank r only
+    KIND_FUSED_AG = 2,   // copy chunk r of rank r to every other rank
+    KIND_RS_STEP = 3,    // one ReduceScatter step of the ring
+    KIND_AG_STEP = 4,    // one AllGather step of the ring
+    KIND_TREE_STEP = 5,  // one recursive-doubling step
+};
+
+struct Plan {
+    Kind kind;
+    ar_dtype dtype;
+    ar_op op;
+    int nranks;
+    size_t count;
+    int step;           // step index for the *_STEP kinds
+    bool vec;           // 16-byte path (all buffers share their address mod 16)
+    unsigned mis;       // that common address mod 16, in bytes
+};
+
+// Grid / block shape a plan launches with (for logging and tests).
+struct Shape {
+    unsigned blocks;
+    unsigned threads;
+    unsigned tiles;     // tiles per chunk (or per pair for the tree)
+};
+
+// Returns false if the plan cannot be launched (grid too large).
+bool plan_shape(const Plan& p, Shape* out);
+
+hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream);
+
+// 16-byte vector copy of `bytes` (multiple of 16, both pointers 16-byte aligned).
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace arlib

@@ -1,0 +1,188 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times.
+
+Where the oracle finishes in seconds it runs on the whole input (4-rank
+int32, the 25 MiB DDP bucket, the two small sweep points); elsewhere it
+computes sampled positions one by one (random positions plus the
+neighbourhood of every chunk boundary, where heads, tails and straddling
+16-byte units live), and whole-array properties are checked on the GPU: all
+ranks identical, fused == per-step bitwise, exact integer / max results
+against an independent torch reduction.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_allreduce_rs_amd as ar
+import workloads as W
+from tests.gpu_helpers import (assert_bits_equal, chunk_ids, gather, sample_positions, to_gpu,
+                               to_np)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run(ts, op, algo):
+    ar.allreduce(ts, op=op, algo=algo)
+    torch.cuda.synchronize()
+
+
+def clone_all(ts):
+    return [t.clone() for t in ts]
+
+
+def ranks_identical(ts):
+    return all(torch.equal(t, ts[0]) for t in ts[1:])
+
+
+def test_small_int32_config():
+    w = W.SMALL_INT
+    xs = W.host_inputs(w, seed=0)
+    assert [ln for _, ln in oracle.chunk_layout(w.count, w.nranks)] == [256] * 4
+    want = oracle.simulate_ring_allreduce(xs, "int32", "sum").state
+    exact = oracle.exact_int_sum(xs)
+    for algo in ("ring_step", "ring_fused", "tree"):
+        ts = to_gpu(xs, "int32")
+        run(ts, "sum", algo)
+        for r in range(w.nranks):
+            assert_bits_equal(to_np(ts[r]), want[r], f"{algo} rank {r}")
+            assert_bits_equal(to_np(ts[r]), exact, f"{algo} exact rank {r}")
+
+
+def test_three_rank_scalar_config():
+    w = W.THREE_RANK
+    xs = W.host_inputs(w, seed=0)
+    for algo in ("ring_step", "ring_fused"):
+        ts = to_gpu(xs, "int32")
+        run(ts, "sum", algo)
+        for t in ts:
+            assert to_np(t).tolist() == [6]
+
+
+def test_ddp_bucket_config_full_oracle():
+    """8 ranks x 6,553,600 fp32 ~ N(0, 1e-3), AVG: whole-vector bitwise parity."""
+    w = W.DDP_BUCKET
+    xs = W.host_inputs(w, seed=0)
+    say("ddp bucket: oracle")
+    want = oracle.simulate_ring_allreduce(xs, "float32", "avg").state[0]
+    f64 = oracle.fp64_sum(xs, "float32") / w.nranks
+    bound = w.nranks * 2.0 ** -24 * np.abs(np.stack(xs).astype(np.float64)).sum(axis=0) / w.nranks
+    for algo in ("ring_fused", "ring_step"):
+        say(f"ddp bucket: {algo}")
+        ts = to_gpu(xs, "float32")
+        run(ts, "avg", algo)
+        assert ranks_identical(ts)
+        got = to_np(ts[0])
+        assert_bits_equal(got, want, algo)
+        assert (np.abs(got.astype(np.float64) - f64) <= bound + 2.0 ** -149).all()
+    tw = oracle.simulate_tree_allreduce(xs, "float32", "avg").state[0]
+    ts = to_gpu(xs, "float32")
+    run(ts, "avg", "tree")
+    assert ranks_identical(ts)
+    assert_bits_equal(to_np(ts[0]), tw, "tree")
+
+
+@pytest.mark.slow
+def test_bf16_2gib_config():
+    """8 ranks x 2^30 bf16 ~ N(0, 1e-2), SUM with a bf16 rounding per hop."""
+    w = W.BF16_2GIB
+    say("bf16 2GiB: generate")
+    a = W.device_inputs(w, seed=0)
+    idx = sample_positions(w.count, w.nranks, k=8192, seed=1)
+    vals = gather(a, idx)
+    b = clone_all(a)
+    say("bf16 2GiB: ring_step")
+    run(a, "sum", "ring_step")
+    say("bf16 2GiB: ring_fused")
+    run(b, "sum", "ring_fused")
+    for r in range(w.nranks):
+        assert torch.equal(a[r], b[r]), f"fused != step on rank {r}"
+    assert ranks_identical(a)
+    want = oracle.ring_fold_at(vals, chunk_ids(idx, w.count, w.nranks), w.nranks, "bfloat16", "sum")
+    assert_bits_equal(gather(a[:1], idx)[0], want, "sampled positions")
+    # bf16 bound: (N-1) hops of an fp32 add then a bf16 rounding
+    f = oracle.bf16_to_f32(vals).astype(np.float64)
+    up = 2.0 ** -8 + 2.0 ** -24 + 2.0 ** -32
+    gamma = (w.nranks - 1) * up / (1 - (w.nranks - 1) * up)
+    err = np.abs(oracle.bf16_to_f32(want).astype(np.float64) - f.sum(axis=0))
+    assert (err <= gamma * np.abs(f).sum(axis=0)).all()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w", W.SWEEP, ids=[w.name for w in W.SWEEP])
+def test_sweep_config(w):
+    """64 ranks, fp32 U[-1,1], SUM: ring (per step and fused) and tree."""
+    say(f"sweep {w.name}")
+    full = w.count <= 16384
+    if full:
+        xs = W.host_inputs(w, seed=0)
+        a = to_gpu(xs, "float32")
+    else:
+        a = W.device_inputs(w, seed=0)
+        idx = sample_positions(w.count, w.nranks, k=4096, seed=2)
+        vals = gather(a, idx)
+    b, c = clone_all(a), clone_all(a)
+    run(a, "sum", "ring_step")
+    run(b, "sum", "ring_fused")
+    run(c, "sum", "tree")
+    for r in range(w.nranks):
+        assert torch.equal(a[r], b[r]), f"fused != step on rank {r}"
+    assert ranks_identical(a) and ranks_identical(c)
+    if full:
+        assert_bits_equal(to_np(a[0]), oracle.simulate_ring_allreduce(xs, "float32", "sum").state[0],
+                          "ring")
+        assert_bits_equal(to_np(c[0]), oracle.simulate_tree_allreduce(xs, "float32", "sum").state[0],
+                          "tree")
+    else:
+        ring_want = oracle.ring_fold_at(vals, chunk_ids(idx, w.count, w.nranks), w.nranks,
+                                        "float32", "sum")
+        tree_want = oracle.tree_fold_at(vals, "float32", "sum")
+        assert_bits_equal(gather(a[:1], idx)[0], ring_want, "ring sampled")
+        assert_bits_equal(gather(c[:1], idx)[0], tree_want, "tree sampled")
+    del a, b, c
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("w", [W.RAGGED_MAX, W.RAGGED_INT], ids=lambda w: w.name)
+def test_ragged_config(w):
+    """16 ranks x 268,435,459 elements (ragged last chunk; chunk starts cycle
+    through 16-byte misalignments 0, 4, 8, 12)."""
+    say(f"ragged {w.name}: generate")
+    lay = oracle.chunk_layout(w.count, w.nranks)
+    assert [ln for _, ln in lay] == [16_777_217] * 15 + [16_777_204]
+    a = W.device_inputs(w, seed=0)
+    idx = sample_positions(w.count, w.nranks, k=8192, seed=3)
+    vals = gather(a, idx)
+    # independent whole-array reference computed by torch before the call
+    if w.op == "max":
+        ref = a[0].clone()
+        for t in a[1:]:
+            ref = torch.maximum(ref, t)
+    else:
+        acc = torch.zeros(w.count, dtype=torch.int64, device="cuda")
+        for t in a:
+            acc += t.to(torch.int64)
+        ref = acc.to(torch.int32)
+        del acc
+    b = clone_all(a)
+    say(f"ragged {w.name}: ring_fused")
+    run(a, w.op, "ring_fused")
+    say(f"ragged {w.name}: ring_step")
+    run(b, w.op, "ring_step")
+    for r in range(w.nranks):
+        assert torch.equal(a[r], ref), f"rank {r} differs from the whole-array reference"
+        assert torch.equal(b[r], ref), f"ring_step rank {r} differs"
+    want = (oracle.exact_max(vals, w.dtype) if w.op == "max" else oracle.exact_int_sum(vals))
+    assert_bits_equal(gather(a[:1], idx)[0], want, "sampled positions")
+    del a, b, ref
+    torch.cuda.empty_cache()

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bitwise equality for every dtype -- int32 and MAX are exact, and fp32 /
+bf16 SUM follow the same ring order (or pairwise tree order) with the same
+per-hop rounding as the oracle.  The fused ring must also stay within
+N * 2^-24 * sum|x| of the binary64 sum (checked in test_gpu_configs.py).
+Sizes here span several 2048-element tiles per chunk and ragged tails.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_allreduce_rs_amd as ar
+from tests.gpu_helpers import assert_bits_equal, to_gpu, to_np
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DT_OPS = [("int32", "sum"), ("int32", "max"), ("float32", "sum"), ("float32", "max"),
+          ("float32", "avg"), ("bfloat16", "sum"), ("bfloat16", "max"), ("bfloat16", "avg")]
+
+
+def rand_inputs(dtype, n, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if dtype == "int32":
+        return [rng.integers(-2**31, 2**31, size=count, dtype=np.int64).astype(np.int32)
+                for _ in range(n)]
+    f = [(rng.standard_normal(count) * rng.choice([1e-3, 1.0, 1e3])).astype(np.float32)
+         for _ in range(n)]
+    if dtype == "float32":
+        return f
+    import torch as _t
+    return [_t.from_numpy(x).to(_t.bfloat16).view(_t.int16).numpy().view(np.uint16) for x in f]
+
+
+SIZES = [(1, 5), (2, 1), (2, 4099), (3, 1), (3, 3), (3, 10007), (4, 6), (4, 24581),
+         (5, 4), (5, 9), (7, 30011), (8, 1), (8, 65539), (16, 33), (16, 40003)]
+
+
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("n,count", SIZES)
+def test_ring_allreduce_matches_oracle(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n * 7919 + count)
+    want = oracle.simulate_ring_allreduce(xs, dtype, op).state
+    for algo in ("ring_step", "ring_fused"):
+        ts = to_gpu(xs, dtype)
+        ar.allreduce(ts, op=op, algo=algo)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), want[r], f"{algo} {dtype} {op} n={n} count={count} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("n,count", [(1, 7), (2, 4099), (4, 6), (4, 24581), (8, 65539),
+                                     (16, 33), (16, 40003), (32, 2050)])
+def test_tree_allreduce_matches_oracle(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n * 31 + count)
+    want = oracle.simulate_tree_allreduce(xs, dtype, op).state
+    ts = to_gpu(xs, dtype)
+    ar.allreduce(ts, op=op, algo="tree")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), want[r], f"tree {dtype} {op} n={n} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "max")])
+@pytest.mark.parametrize("n,count", [(3, 10007), (5, 9), (8, 65539), (4, 6)])
+def test_every_ring_step_matches_oracle_snapshot(dtype, op, n, count):
+    """After each of the 2(N-1) steps the whole state (written and untouched
+    chunks alike) equals the oracle's state after the same step."""
+    xs = rand_inputs(dtype, n, count, seed=count)
+    snaps = oracle.simulate_ring_allreduce(xs, dtype, op, record=True).snapshots
+    assert len(snaps) == 2 * (n - 1)
+    ts = to_gpu(xs, dtype)
+    for k in range(n - 1):
+        ar.ring_rs_step(ts, op, k)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), snaps[k][r], f"RS step {k} rank {r}")
+    for k in range(n - 1):
+        ar.ring_ag_step(ts, k)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), snaps[n - 1 + k][r], f"AG step {k} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "sum")])
+@pytest.mark.parametrize("n,count", [(4, 24581), (8, 1000), (16, 40003)])
+def test_every_tree_step_matches_oracle_snapshot(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=count + 1)
+    snaps = oracle.simulate_tree_allreduce(xs, dtype, op, record=True).snapshots
+    ts = to_gpu(xs, dtype)
+    for s in range(len(snaps)):
+        ar.tree_step(ts, op, s)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), snaps[s][r], f"tree step {s} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("algo", ["ring_step", "ring_fused"])
+@pytest.mark.parametrize("n,count", [(3, 10007), (4, 6), (8, 65539), (16, 40003)])
+def test_reduce_scatter_then_allgather(dtype, op, algo, n, count):
+    xs = rand_inputs(dtype, n, count, seed=count * 3 + n)
+    direct = oracle.ordered_ring_fold(xs, dtype, op)
+    ts = to_gpu(xs, dtype)
+    ar.reduce_scatter(ts, op=op, algo=algo)
+    torch.cuda.synchronize()
+    lay = oracle.chunk_layout(count, n)
+    for r in range(n):
+        lo, ln = lay[r]
+        assert ar.chunk_range(count, n, r) == (lo, ln)
+        assert_bits_equal(to_np(ts[r])[lo:lo + ln], direct[lo:lo + ln], f"RS {algo} rank {r}")
+    ar.allgather(ts, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), direct, f"RS+AG {algo} rank {r}")
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bfloat16"])
+@pytest.mark.parametrize("n,count", [(3, 10007), (8, 65539), (5, 9)])
+def test_allgather_copies_owner_chunks(dtype, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n + count)
+    want = oracle.simulate_ring_allgather(xs, dtype).state
+    for algo in ("ring_step", "ring_fused"):
+        ts = to_gpu(xs, dtype)
+        ar.allgather(ts, algo=algo)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), want[r], f"AG {algo} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "sum")])
+@pytest.mark.parametrize("shift", [0, 1, 2, 3, 5])
+@pytest.mark.parametrize("same_alignment", [True, False])
+def test_unaligned_buffers(dtype, op, shift, same_alignment):
+    """Buffers that start off a 16-byte boundary: a common misalignment takes
+    the vector path with element-wise heads and tails, mixed misalignments the
+    element-wise path.  Both must equal the oracle bitwise."""
+    n, count = 5, 12345
+    xs = rand_inputs(dtype, n, count, seed=shift + 17)
+    want = oracle.simulate_ring_allreduce(xs, dtype, op).state
+    stride = ((count + 64 + 7) // 8) * 8          # a multiple of 16 bytes per row
+    for algo in ("ring_step", "ring_fused"):
+        store = torch.zeros(n * stride, dtype=to_gpu(xs[:1], dtype)[0].dtype, device="cuda")
+        views = []
+        for r in range(n):
+            off = r * stride + (shift if same_alignment else (shift + r) % 8)
+            v = store[off:off + count]
+            v.copy_(to_gpu([xs[r]], dtype)[0])
+            views.append(v)
+        guard = store.clone()
+        ar.allreduce(views, op=op, algo=algo)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(views[r]), want[r], f"{algo} shift {shift} rank {r}")
+        # nothing outside the rank views was touched
+        mask = torch.ones_like(store, dtype=torch.bool)
+        for r in range(n):
+            off = r * stride + (shift if same_alignment else (shift + r) % 8)
+            mask[off:off + count] = False
+        assert torch.equal(store[mask], guard[mask])
+
+
+def test_sides_are_not_shared_state():
+    """Two contexts on different streams give the same bits."""
+    xs = rand_inputs("float32", 4, 5000, seed=1)
+    want = oracle.simulate_ring_allreduce(xs, "float32", "avg").state
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ts = to_gpu(xs, "float32")
+        ar.allreduce(ts, op="avg", algo="ring_fused")
+    s.synchronize()
+    for r in range(4):
+        assert_bits_equal(to_np(ts[r]), want[r], "side stream")
