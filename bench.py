@@ -1,0 +1,297 @@
+"""Benchmark of the single-GPU AllReduce hot path on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--algo ALGO]
+
+One step is one in-place AllReduce (ReduceScatter + AllGather, fused into one
+pass by default) of N logical ranks held in HBM.  The default workload is the
+DDP gradient bucket: 8 ranks x 25 MiB fp32 (6,553,600 values ~ N(0, 1e-3)),
+op AVG.  Steps rotate over several independent bucket sets whose combined
+footprint is several times the 256 MB Infinity Cache, so every step reads its
+inputs from HBM, as a DDP step reducing many different buckets does.
+
+Printed (one JSON line):
+  value      algorithmic HBM GB/s of the whole timed run: 2*N*K bytes per
+             AllReduce (every input read once, every output written once; K =
+             bytes per rank) x K steps / wall time between the two
+             synchronisations
+  roofline   the dominant kernel's GB/s from HIP events recorded on its stream
+             at both ends of the timed region (mean per launch), against the
+             8 TB/s HBM peak; `traffic` is the
+             HBM bytes per launch measured with rocprofv3 counters (scaled by a
+             plain copy of known size) when the kernel source is unchanged
+             since they were taken, else null
+  cpu_baseline  the CPU oracle (message-passing ring simulation, numpy, one
+             core) on the same workload, rank 0 only
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+INFINITY_CACHE_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_rs_amd", "csrc", f)
+                  for f in ("kernels.hip", "elem.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from the committed counter runs, if still valid."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(key)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def parse():
+    import workloads as W
+    names = {w.name: w for w in W.ALL}
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default=W.DDP_BUCKET.name, choices=sorted(names))
+    ap.add_argument("--algo", default="ring_fused", choices=["ring_fused", "ring_step", "tree"])
+    ap.add_argument("--sets", type=int, default=0,
+                    help="bucket sets to rotate over (0: enough to exceed the Infinity Cache 4x)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the secondary per-step ring / tree / copy measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent timing the oracle")
+    a = ap.parse_args()
+    return a, names[a.workload]
+
+
+def time_algo(ar, sets, w, algo, steps, warmup):
+    """Time `steps` back-to-back launches.
+
+    Returns (wall seconds between the two synchronisations, mean ms per
+    launch from HIP events recorded on the launch stream at the start and the
+    end of the timed region)."""
+    import torch
+    calls = [ar.bind(ts, op=w.op, algo=algo) for ts in sets]
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        calls[i % len(calls)]()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / steps
+
+
+def copy_ceiling(ar, nbytes, reps=50):
+    """GB/s (read + write) of the plain 16-byte copy kernel over nbytes,
+    rotating over buffer pairs that together exceed the Infinity Cache."""
+    import torch
+    nb = (nbytes // 16) * 16
+    npairs = max(2, -(-4 * INFINITY_CACHE_BYTES // (2 * nb)))
+    pairs = [(torch.empty(nb, dtype=torch.uint8, device="cuda"),
+              torch.empty(nb, dtype=torch.uint8, device="cuda")) for _ in range(npairs)]
+    for d, s in pairs:
+        s.fill_(1)
+        ar.copy_(d, s)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(reps):
+        d, s = pairs[i % len(pairs)]
+        ar.copy_(d, s)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    return 2 * nb / (ms * 1e-3) / 1e9, ms
+
+
+def cpu_baseline(w, sets_host, gpu_first, min_seconds):
+    """Time the CPU oracle on the workload; also check the GPU's first result."""
+    import numpy as np
+    import oracle
+    reps, t_total = 0, 0.0
+    out = None
+    while t_total < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        out = oracle.simulate_ring_allreduce(sets_host, w.dtype, w.op).state
+        t_total += time.perf_counter() - t0
+        reps += 1
+    ok = all(np.array_equal(np.ascontiguousarray(g).view(np.uint8),
+                            np.ascontiguousarray(o).view(np.uint8))
+             for g, o in zip(gpu_first, out))
+    per = t_total / reps
+    gbps = 2 * w.nranks * w.bytes_per_rank / per / 1e9
+    return {
+        "value": round(gbps, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"whole workload ({w.nranks} ranks x {w.count} {w.dtype}, {w.op}) through "
+                   f"oracle.simulate_ring_allreduce, {reps} run(s), {per:.3f} s each; numpy "
+                   "elementwise kernels, single thread"),
+        "seconds_per_allreduce": round(per, 4),
+    }, ok
+
+
+DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
+METRIC = "AllReduce GB/s + % of HBM peak, N=8 ranks \u00d7 25 MB fp32, 1 MI355X"
+
+
+def step_bytes(w, algo):
+    """HBM bytes one AllReduce moves with each algorithm (K = bytes per rank)."""
+    n, k = w.nranks, w.bytes_per_rank
+    if algo == "ring_fused":
+        return 2 * n * k                      # N*K read + N*K written
+    if algo == "ring_step":
+        return 5 * (n - 1) * k                # (N-1) x (2K read + K written) + (N-1) x 2K
+    return 2 * n * k * (n.bit_length() - 1)   # log2 N steps of 2*N*K
+
+
+def main():
+    args, w = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every logical rank lives in one GPU's HBM, so "
+              f"--gpus {args.gpus} is not a configuration of this path (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import ring_allreduce_rs_amd as ar
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.algo == "tree" and w.nranks & (w.nranks - 1):
+        print("tree needs a power-of-two rank count", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    set_bytes = w.nranks * w.bytes_per_rank
+    nsets = args.sets or max(2, -(-4 * INFINITY_CACHE_BYTES // set_bytes))
+    nsets = max(1, min(nsets, (64 << 30) // max(set_bytes, 1)))
+    host = W.host_inputs(w, seed=args.seed) if set_bytes <= (1 << 30) else None
+    torch_dt = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}[w.dtype]
+
+    def upload(x):
+        if w.dtype == "bfloat16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(x).to("cuda")
+
+    def download(t):
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    sets = []
+    for s in range(nsets):
+        if s == 0 and host is not None:
+            sets.append([upload(x) for x in host])
+        else:
+            sets.append(W.device_inputs(w, seed=args.seed + s))
+    assert all(t.dtype == torch_dt for ts in sets for t in ts)
+
+    # first AllReduce of set 0, kept for the parity check in the CPU leg
+    ar.allreduce(sets[0], op=w.op, algo=args.algo)
+    torch.cuda.synchronize()
+    gpu_first = [download(t) for t in sets[0]] if host is not None else None
+
+    wall, ms = time_algo(ar, sets, w, args.algo, args.steps, args.warmup)
+    alg_bytes = 2 * w.nranks * w.bytes_per_rank
+    value = alg_bytes * args.steps / wall / 1e9
+    t_step = wall / args.steps
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    key = f"{w.name}/{args.algo}"
+    traffic = measured_traffic(key)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_TAG[w.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "nranks": w.nranks, "count_per_rank": w.count,
+            "bytes_per_rank": w.bytes_per_rank, "op": w.op, "algo": args.algo,
+            "distribution": list(w.dist), "rotating_sets": nsets, "seed": args.seed,
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "algbw_GBps": round(w.bytes_per_rank / t_step / 1e9, 2),
+        "busbw_GBps": round(2 * (w.nranks - 1) / w.nranks * w.bytes_per_rank / t_step / 1e9, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": {"ring_fused": "k_fused", "ring_step": "k_rs_step/k_ag_step",
+                       "tree": "k_tree_step"}[args.algo],
+            "us_per_launch": round(ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+        "gpu": torch.cuda.get_device_properties(0).name,
+    }
+    if not args.no_others:
+        others = {}
+        for algo in ("ring_fused", "ring_step", "tree"):
+            if algo == args.algo or (algo == "tree" and w.nranks & (w.nranks - 1)):
+                continue
+            reps = max(5, min(args.steps // 4, 100))
+            wl, m = time_algo(ar, sets, w, algo, reps, 3)
+            others[algo] = {
+                "us_per_allreduce": round(wl / reps * 1e6, 2),
+                "GBps_algorithmic": round(alg_bytes * reps / wl / 1e9, 2),
+                "GBps_bytes_moved": round(step_bytes(w, algo) * reps / wl / 1e9, 2),
+                "event_us_per_allreduce": round(m * 1e3, 2),
+            }
+        cg, cms = copy_ceiling(ar, w.nranks * w.bytes_per_rank)
+        others["copy_ceiling"] = {"GBps": round(cg, 2), "bytes": 2 * w.nranks * w.bytes_per_rank,
+                                  "us": round(cms * 1e3, 2)}
+        out["others"] = others
+    if not args.no_cpu_baseline and host is not None:
+        cb, ok = cpu_baseline(w, host, gpu_first, args.cpu_seconds)
+        cb["host_cpus"] = os.cpu_count()
+        out["cpu_baseline"] = cb
+        out["parity_vs_oracle"] = "bitwise" if ok else "MISMATCH"
+    elif not args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,6 +1,7 @@
 """Build libar.so (HIP kernels + C ABI) in-tree for gfx950.
 
-Run ``python -m ring_allreduce_rs_amd._build`` or ``__graft_entry__.build()``.
+Run ``python ring_allreduce_rs_amd/_build.py`` or ``__graft_entry__.build()``
+(the script does not import the package, which needs the library).
 hipcc cross-compiles for gfx950 without a GPU present.
 """
 
@@ -61,4 +62,4 @@ def build(verbose: bool = False, extra_flags=None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, extra_flags=sys.argv[1:]))

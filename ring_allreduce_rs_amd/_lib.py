@@ -46,7 +46,7 @@ class ArError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m ring_allreduce_rs_amd._build` "
+            f"{LIB_PATH} is not built; run `python ring_allreduce_rs_amd/_build.py` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i, cp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_char_p

@@ -49,14 +49,23 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_widen(uint32_t h) { return as_f32(h << 16); }
 
+// x / n, correctly rounded.  When n is a power of two the caller passes
+// inv = 1/n (exact); x * 2^-k and x / 2^k are then the same real number
+// rounded once, so the product is the correctly rounded quotient, subnormal
+// results included (denormals are not flushed).  Otherwise inv is 0 and the
+// IEEE division is used.
+__device__ __forceinline__ float div_by_n(float x, float nf, float inv) {
+    return inv != 0.0f ? __fmul_rn(x, inv) : __fdiv_rn(x, nf);
+}
+
 // Every op exposes: element size, one-element combine/finish on the low bits
 // of a word, and whole-word combine/finish (two bf16 per word).
 struct OpI32Sum {
     static constexpr int kElemBytes = 4;
     __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) { return a + b; }
-    __device__ static uint32_t finish_elem(uint32_t a, float) { return a; }
+    __device__ static uint32_t finish_elem(uint32_t a, float, float) { return a; }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return a + b; }
-    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+    __device__ static uint32_t finish_word(uint32_t a, float, float) { return a; }
 };
 
 struct OpI32Max {
@@ -64,9 +73,9 @@ struct OpI32Max {
     __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) {
         return (int32_t)a > (int32_t)b ? a : b;
     }
-    __device__ static uint32_t finish_elem(uint32_t a, float) { return a; }
+    __device__ static uint32_t finish_elem(uint32_t a, float, float) { return a; }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return comb_elem(a, b); }
-    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+    __device__ static uint32_t finish_word(uint32_t a, float, float) { return a; }
 };
 
 struct OpF32Sum {
@@ -74,19 +83,21 @@ struct OpF32Sum {
     __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) {
         return as_u32(__fadd_rn(as_f32(a), as_f32(b)));
     }
-    __device__ static uint32_t finish_elem(uint32_t a, float nf) {
-        return as_u32(__fdiv_rn(as_f32(a), nf));
+    __device__ static uint32_t finish_elem(uint32_t a, float nf, float inv) {
+        return as_u32(div_by_n(as_f32(a), nf, inv));
     }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return comb_elem(a, b); }
-    __device__ static uint32_t finish_word(uint32_t a, float nf) { return finish_elem(a, nf); }
+    __device__ static uint32_t finish_word(uint32_t a, float nf, float inv) {
+        return finish_elem(a, nf, inv);
+    }
 };
 
 struct OpF32Max {
     static constexpr int kElemBytes = 4;
     __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) { return fmaximum_bits(a, b); }
-    __device__ static uint32_t finish_elem(uint32_t a, float) { return a; }
+    __device__ static uint32_t finish_elem(uint32_t a, float, float) { return a; }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return fmaximum_bits(a, b); }
-    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+    __device__ static uint32_t finish_word(uint32_t a, float, float) { return a; }
 };
 
 struct OpBF16Sum {
@@ -94,14 +105,14 @@ struct OpBF16Sum {
     __device__ static uint32_t comb_elem(uint32_t a, uint32_t b) {
         return bf16_rne(__fadd_rn(bf16_widen(a & 0xffffu), bf16_widen(b & 0xffffu)));
     }
-    __device__ static uint32_t finish_elem(uint32_t a, float nf) {
-        return bf16_rne(__fdiv_rn(bf16_widen(a & 0xffffu), nf));
+    __device__ static uint32_t finish_elem(uint32_t a, float nf, float inv) {
+        return bf16_rne(div_by_n(bf16_widen(a & 0xffffu), nf, inv));
     }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) {
         return comb_elem(a, b) | (comb_elem(a >> 16, b >> 16) << 16);
     }
-    __device__ static uint32_t finish_word(uint32_t a, float nf) {
-        return finish_elem(a, nf) | (finish_elem(a >> 16, nf) << 16);
+    __device__ static uint32_t finish_word(uint32_t a, float nf, float inv) {
+        return finish_elem(a, nf, inv) | (finish_elem(a >> 16, nf, inv) << 16);
     }
 };
 
@@ -112,11 +123,11 @@ struct OpBF16Max {
         const uint32_t m = fmaximum_bits((a & 0xffffu) << 16, (b & 0xffffu) << 16);
         return m >> 16;
     }
-    __device__ static uint32_t finish_elem(uint32_t a, float) { return a & 0xffffu; }
+    __device__ static uint32_t finish_elem(uint32_t a, float, float) { return a & 0xffffu; }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) {
         return comb_elem(a, b) | (comb_elem(a >> 16, b >> 16) << 16);
     }
-    __device__ static uint32_t finish_word(uint32_t a, float) { return a; }
+    __device__ static uint32_t finish_word(uint32_t a, float, float) { return a; }
 };
 
 // Copy-only "op" for the AllGather paths (element size matters, values do not).
@@ -166,12 +177,12 @@ __device__ __forceinline__ u32x4 comb4(u32x4 a, u32x4 b) {
 }
 
 template <class Op>
-__device__ __forceinline__ u32x4 finish4(u32x4 a, float nf) {
+__device__ __forceinline__ u32x4 finish4(u32x4 a, float nf, float inv) {
     u32x4 r;
-    r.x = Op::finish_word(a.x, nf);
-    r.y = Op::finish_word(a.y, nf);
-    r.z = Op::finish_word(a.z, nf);
-    r.w = Op::finish_word(a.w, nf);
+    r.x = Op::finish_word(a.x, nf, inv);
+    r.y = Op::finish_word(a.y, nf, inv);
+    r.z = Op::finish_word(a.z, nf, inv);
+    r.w = Op::finish_word(a.w, nf, inv);
     return r;
 }
 

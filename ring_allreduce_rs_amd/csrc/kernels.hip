@@ -39,10 +39,38 @@
 
 namespace arlib {
 
-constexpr int kThreads = 256;  // 4 wavefronts of 64
-constexpr int kUnroll = 2;     // 16-byte units per lane per tile
-constexpr int kBatch = 8;      // ranks of loads issued before they are folded
-constexpr bool kNonTemporal = false;
+#ifndef AR_FUSED_NT
+#define AR_FUSED_NT 1
+#endif
+#ifndef AR_STEP_NT
+#define AR_STEP_NT 0
+#endif
+
+#ifndef AR_FUSED_THREADS
+#define AR_FUSED_THREADS 256
+#endif
+#ifndef AR_FUSED_UNROLL
+#define AR_FUSED_UNROLL 2
+#endif
+#ifndef AR_SPECIALIZE_N
+#define AR_SPECIALIZE_N 1
+#endif
+
+constexpr int kThreads = 256;       // per-step kernels: 4 wavefronts of 64
+constexpr int kUnroll = 2;          // per-step kernels: 16-byte units per lane per tile
+constexpr int kFusedThreads = AR_FUSED_THREADS;
+constexpr int kFusedUnroll = AR_FUSED_UNROLL;
+constexpr int kBatch = 8;           // ranks of loads issued before they are folded
+constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
+// Streaming (non-temporal) loads and stores.  The fused kernel touches every
+// byte once, so caching it only evicts useful lines: on MI355X 8 x 25 MiB went
+// from 86 us to 77 us with both loads and stores streaming.  The per-step
+// kernels are the opposite case: each step re-reads what the previous step
+// wrote, and a 200 MiB working set stays in the 256 MB Infinity Cache when
+// the stores are ordinary (ring 8 x 25 MiB: 169 us with, 189 us without).
+constexpr bool kFusedNT = AR_FUSED_NT != 0;
+constexpr bool kStepNT = AR_STEP_NT != 0;
+constexpr int kCopyUnroll = 1;  // the plain copy streams best with one unit per lane
 
 struct Args {
     RankTable t;
@@ -54,30 +82,31 @@ struct Args {
     unsigned mis;     // every buffer's address mod 16, in bytes
     int avg;          // 1: divide the finished sum by n
     float nf;         // (float)n
+    float inv;        // 1/n when n is a power of two (exact), else 0
 };
 
-template <class Op, bool VEC>
+template <class Op, bool VEC, bool NT = false>
 struct Unit;
 
-template <class Op>
-struct Unit<Op, true> {
+template <class Op, bool NT>
+struct Unit<Op, true, NT> {
     using T = u32x4;
     static constexpr int kBytes = 16;
-    __device__ static T ld(const char* p) { return ld16<kNonTemporal>(p); }
-    __device__ static void st(char* p, T v) { st16<kNonTemporal>(p, v); }
+    __device__ static T ld(const char* p) { return ld16<NT>(p); }
+    __device__ static void st(char* p, T v) { st16<NT>(p, v); }
     __device__ static T comb(T a, T b) { return comb4<Op>(a, b); }
-    __device__ static T fin(T a, float nf) { return finish4<Op>(a, nf); }
+    __device__ static T fin(T a, float nf, float inv) { return finish4<Op>(a, nf, inv); }
     __device__ static T zero() { return u32x4{0u, 0u, 0u, 0u}; }
 };
 
-template <class Op>
-struct Unit<Op, false> {
+template <class Op, bool NT>
+struct Unit<Op, false, NT> {
     using T = uint32_t;
     static constexpr int kBytes = Op::kElemBytes;
     __device__ static T ld(const char* p) { return ld_elem<Op::kElemBytes>(p); }
     __device__ static void st(char* p, T v) { st_elem<Op::kElemBytes>(p, v); }
     __device__ static T comb(T a, T b) { return Op::comb_elem(a, b); }
-    __device__ static T fin(T a, float nf) { return Op::finish_elem(a, nf); }
+    __device__ static T fin(T a, float nf, float inv) { return Op::finish_elem(a, nf, inv); }
     __device__ static T zero() { return 0u; }
 };
 
@@ -129,47 +158,52 @@ __device__ __forceinline__ char* rank_ptr(const Args& a, int r) {
 
 // ---------------------------------------------------------------- fused ring
 
-// Units ubase, ubase+kThreads, ... (kUnroll of them, bounded by `units`) of
-// the range starting at byte offset byte0 in every rank buffer.
-template <class Op, int MODE, bool VEC>
+// Units ubase, ubase+kFusedThreads, ... (kFusedUnroll of them, bounded by
+// `units`) of the range starting at byte offset byte0 in every rank buffer.
+// NR > 0 fixes the rank count at compile time (loops fully unrolled); NR == 0
+// reads it from the arguments.
+template <class Op, int MODE, bool VEC, int NR>
 __device__ __forceinline__ void fused_units(const Args& a, int c, int start, size_t byte0,
                                             size_t ubase, size_t units) {
-    using X = Unit<Op, VEC>;
+    using X = Unit<Op, VEC, kFusedNT>;
     using T = typename X::T;
-    const int n = a.n;
-    bool ok[kUnroll];
-    size_t off[kUnroll];
+    constexpr int U = kFusedUnroll;
+    const int n = NR > 0 ? NR : a.n;
+    bool ok[U];
+    size_t off[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const size_t idx = ubase + (size_t)u * kThreads;
+    for (int u = 0; u < U; ++u) {
+        const size_t idx = ubase + (size_t)u * kFusedThreads;
         ok[u] = idx < units;
         off[u] = byte0 + idx * X::kBytes;
     }
-    T acc[kUnroll];
+    T acc[U];
     if constexpr (MODE == KIND_FUSED_AG) {
         const char* src = rank_ptr(a, c);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc[u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+        for (int u = 0; u < U; ++u) acc[u] = ok[u] ? X::ld(src + off[u]) : X::zero();
         for (int r = 0; r < n; ++r) {
             if (r == c) continue;
             char* dst = rank_ptr(a, r);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < U; ++u)
                 if (ok[u]) X::st(dst + off[u], acc[u]);
         }
         return;
     } else {
         // ring order: start = c+1, then c+2, ..., ending with c itself
         int r = start;
-        for (int j0 = 0; j0 < n; j0 += kBatch) {
-            T v[kBatch][kUnroll];
+#pragma unroll
+        for (int j0 = 0; j0 < (NR > 0 ? NR : AR_MAX_RANKS); j0 += kBatch) {
+            if (NR == 0 && j0 >= n) break;
+            T v[kBatch][U];
             int rr = r;
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 if (j0 + j < n) {
                     const char* src = rank_ptr(a, rr);
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u)
+                    for (int u = 0; u < U; ++u)
                         v[j][u] = ok[u] ? X::ld(src + off[u]) : X::zero();
                     rr = (rr + 1 == n) ? 0 : rr + 1;
                 }
@@ -178,7 +212,7 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
             for (int j = 0; j < kBatch; ++j) {
                 if (j0 + j < n) {
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u)
+                    for (int u = 0; u < U; ++u)
                         acc[u] = (j0 + j == 0) ? v[j][u] : X::comb(acc[u], v[j][u]);
                 }
             }
@@ -186,28 +220,30 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
         }
         if (a.avg) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) acc[u] = X::fin(acc[u], a.nf);
+            for (int u = 0; u < U; ++u) acc[u] = X::fin(acc[u], a.nf, a.inv);
         }
         if constexpr (MODE == KIND_FUSED_RS) {
             char* dst = rank_ptr(a, c);
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < U; ++u)
                 if (ok[u]) X::st(dst + off[u], acc[u]);
         } else {
-            for (int r2 = 0; r2 < n; ++r2) {
+#pragma unroll
+            for (int r2 = 0; r2 < (NR > 0 ? NR : AR_MAX_RANKS); ++r2) {
+                if (NR == 0 && r2 >= n) break;
                 char* dst = rank_ptr(a, r2);
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u)
+                for (int u = 0; u < U; ++u)
                     if (ok[u]) X::st(dst + off[u], acc[u]);
             }
         }
     }
 }
 
-template <class Op, int MODE, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_fused(const Args a) {
+template <class Op, int MODE, bool VEC, int NR>
+__global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
     constexpr int EB = Op::kElemBytes;
-    const int n = a.n;
+    const int n = NR > 0 ? NR : a.n;
     const int c = (int)(blockIdx.x / a.tiles);
     const unsigned tile = blockIdx.x - (unsigned)c * a.tiles;
     size_t lo, len;
@@ -215,16 +251,18 @@ __global__ __launch_bounds__(kThreads) void k_fused(const Args a) {
     if (len == 0) return;
     const Span sp = make_span<EB, VEC>(lo, len, a.mis);
     const int start = (c + 1 == n) ? 0 : c + 1;
-    const size_t ubase = (size_t)tile * (kThreads * kUnroll) + threadIdx.x;
+    const size_t ubase = (size_t)tile * (kFusedThreads * kFusedUnroll) + threadIdx.x;
     if (ubase < sp.units)
-        fused_units<Op, MODE, VEC>(a, c, start, sp.body * EB, ubase, sp.units);
+        fused_units<Op, MODE, VEC, NR>(a, c, start, sp.body * EB, ubase, sp.units);
     if constexpr (VEC) {
+        // heads have at most 15 bytes (< 8 elements), as do tails
         if (tile == 0) {
             const unsigned t = threadIdx.x;
             if (t < sp.nhead)
-                fused_units<Op, MODE, false>(a, c, start, (lo + t) * EB, 0, 1);
-            else if (t >= 64 && t - 64 < sp.ntail)
-                fused_units<Op, MODE, false>(a, c, start, (sp.tail + (t - 64)) * EB, 0, 1);
+                fused_units<Op, MODE, false, NR>(a, c, start, (lo + t) * EB, 0, 1);
+            else if (t >= kTailLane && t - kTailLane < sp.ntail)
+                fused_units<Op, MODE, false, NR>(a, c, start, (sp.tail + (t - kTailLane)) * EB,
+                                                 0, 1);
         }
     }
 }
@@ -235,8 +273,8 @@ __global__ __launch_bounds__(kThreads) void k_fused(const Args a) {
 // `both`, src[i] also receives the combination (tree).
 template <class Op, bool VEC, bool REDUCE, bool BOTH>
 __device__ __forceinline__ void pair_units(char* src, char* dst, size_t byte0, size_t ubase,
-                                           size_t units, bool fin, float nf) {
-    using X = Unit<Op, VEC>;
+                                           size_t units, bool fin, float nf, float inv) {
+    using X = Unit<Op, VEC, kStepNT>;
     using T = typename X::T;
     bool ok[kUnroll];
     size_t off[kUnroll];
@@ -257,7 +295,7 @@ __device__ __forceinline__ void pair_units(char* src, char* dst, size_t byte0, s
         T z = x[u];
         if constexpr (REDUCE) {
             z = X::comb(x[u], y[u]);
-            if (fin) z = X::fin(z, nf);
+            if (fin) z = X::fin(z, nf, inv);
         }
         if (ok[u]) {
             X::st(dst + off[u], z);
@@ -268,20 +306,21 @@ __device__ __forceinline__ void pair_units(char* src, char* dst, size_t byte0, s
 
 template <class Op, bool VEC, bool REDUCE, bool BOTH>
 __device__ __forceinline__ void pair_range(char* src, char* dst, size_t lo, size_t len,
-                                           unsigned mis, unsigned tile, bool fin, float nf) {
+                                           unsigned mis, unsigned tile, bool fin, float nf,
+                                           float inv) {
     constexpr int EB = Op::kElemBytes;
     const Span sp = make_span<EB, VEC>(lo, len, mis);
     const size_t ubase = (size_t)tile * (kThreads * kUnroll) + threadIdx.x;
     if (ubase < sp.units)
-        pair_units<Op, VEC, REDUCE, BOTH>(src, dst, sp.body * EB, ubase, sp.units, fin, nf);
+        pair_units<Op, VEC, REDUCE, BOTH>(src, dst, sp.body * EB, ubase, sp.units, fin, nf, inv);
     if constexpr (VEC) {
         if (tile == 0) {
             const unsigned t = threadIdx.x;
             if (t < sp.nhead)
-                pair_units<Op, false, REDUCE, BOTH>(src, dst, (lo + t) * EB, 0, 1, fin, nf);
-            else if (t >= 64 && t - 64 < sp.ntail)
-                pair_units<Op, false, REDUCE, BOTH>(src, dst, (sp.tail + (t - 64)) * EB, 0, 1,
-                                                    fin, nf);
+                pair_units<Op, false, REDUCE, BOTH>(src, dst, (lo + t) * EB, 0, 1, fin, nf, inv);
+            else if (t >= kTailLane && t - kTailLane < sp.ntail)
+                pair_units<Op, false, REDUCE, BOTH>(src, dst, (sp.tail + (t - kTailLane)) * EB, 0,
+                                                    1, fin, nf, inv);
         }
     }
 }
@@ -299,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void k_rs_step(const Args a) {
     if (len == 0) return;
     const bool fin = a.avg && a.step == n - 2;   // the receiver now owns chunk c
     pair_range<Op, VEC, true, false>(rank_ptr(a, r), rank_ptr(a, d), lo, len, a.mis, tile,
-                                     fin, a.nf);
+                                     fin, a.nf, a.inv);
 }
 
 // AllGather step k: rank r forwards chunk (r-k) mod N to rank r+1 unchanged.
@@ -314,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void k_ag_step(const Args a) {
     chunk_bounds(a, c, lo, len);
     if (len == 0) return;
     pair_range<Op, VEC, false, false>(rank_ptr(a, r), rank_ptr(a, d), lo, len, a.mis, tile,
-                                      false, a.nf);
+                                      false, a.nf, a.inv);
 }
 
 // Recursive-doubling step s: pair q is (r, r | 2^s) with bit s of r clear.
@@ -328,22 +367,22 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(const Args a) {
     const int p = r | (1 << s);
     const bool fin = a.avg && (2 << s) == a.n;   // last step
     pair_range<Op, VEC, true, true>(rank_ptr(a, p), rank_ptr(a, r), 0, a.count, a.mis, tile,
-                                    fin, a.nf);
+                                    fin, a.nf, a.inv);
 }
 
 __global__ __launch_bounds__(kThreads) void k_copy(u32x4* __restrict__ dst,
                                                    const u32x4* __restrict__ src, size_t nvec) {
-    const size_t base = (size_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-    u32x4 v[kUnroll];
+    const size_t base = (size_t)blockIdx.x * (kThreads * kCopyUnroll) + threadIdx.x;
+    u32x4 v[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kCopyUnroll; ++u) {
         const size_t i = base + (size_t)u * kThreads;
-        v[u] = i < nvec ? ld16<kNonTemporal>(src + i) : u32x4{0u, 0u, 0u, 0u};
+        v[u] = i < nvec ? ld16<true>(src + i) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kCopyUnroll; ++u) {
         const size_t i = base + (size_t)u * kThreads;
-        if (i < nvec) st16<kNonTemporal>(dst + i, v[u]);
+        if (i < nvec) st16<true>(dst + i, v[u]);
     }
 }
 
@@ -356,7 +395,9 @@ static size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 bool plan_shape(const Plan& p, Shape* out) {
     const size_t eb = (size_t)elem_bytes(p.dtype);
     const size_t epu = p.vec ? 16 / eb : 1;
-    const size_t per_tile = (size_t)kThreads * kUnroll;
+    const bool fused = p.kind == KIND_FUSED_AR || p.kind == KIND_FUSED_RS || p.kind == KIND_FUSED_AG;
+    const size_t threads = fused ? kFusedThreads : kThreads;
+    const size_t per_tile = threads * (fused ? kFusedUnroll : kUnroll);
     size_t tiles, groups;
     if (p.kind == KIND_TREE_STEP) {
         tiles = ceil_div(ceil_div(p.count, epu), per_tile);
@@ -370,9 +411,18 @@ bool plan_shape(const Plan& p, Shape* out) {
     const size_t blocks = tiles * groups;
     if (blocks == 0 || blocks > 0x7fffffffu || tiles > 0xffffffffu) return false;
     out->blocks = (unsigned)blocks;
-    out->threads = kThreads;
+    out->threads = (unsigned)threads;
     out->tiles = (unsigned)tiles;
     return true;
+}
+
+template <class Op, int MODE, bool VEC>
+static void launch_fused(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    const dim3 block(kFusedThreads);
+    if (AR_SPECIALIZE_N && VEC && p.nranks == 8)
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0>), grid, block, 0, s, a);
 }
 
 template <class Op, bool VEC>
@@ -380,10 +430,10 @@ static hipError_t launch_kind(const Plan& p, const Args& a, dim3 grid, hipStream
     const dim3 block(kThreads);
     switch (p.kind) {
         case KIND_FUSED_AR:
-            hipLaunchKernelGGL((k_fused<Op, KIND_FUSED_AR, VEC>), grid, block, 0, s, a);
+            launch_fused<Op, KIND_FUSED_AR, VEC>(p, a, grid, s);
             break;
         case KIND_FUSED_RS:
-            hipLaunchKernelGGL((k_fused<Op, KIND_FUSED_RS, VEC>), grid, block, 0, s, a);
+            launch_fused<Op, KIND_FUSED_RS, VEC>(p, a, grid, s);
             break;
         case KIND_RS_STEP:
             hipLaunchKernelGGL((k_rs_step<Op, VEC>), grid, block, 0, s, a);
@@ -403,7 +453,8 @@ static hipError_t launch_copy_kind(const Plan& p, const Args& a, dim3 grid, hipS
     using Op = OpCopy<EB>;
     switch (p.kind) {
         case KIND_FUSED_AG:
-            hipLaunchKernelGGL((k_fused<Op, KIND_FUSED_AG, VEC>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((k_fused<Op, KIND_FUSED_AG, VEC, 0>), dim3(grid), dim3(kFusedThreads),
+                               0, s, a);
             break;
         case KIND_AG_STEP:
             hipLaunchKernelGGL((k_ag_step<Op, VEC>), grid, block, 0, s, a);
@@ -432,6 +483,7 @@ hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream) {
     a.mis = p.mis;
     a.avg = p.op == AR_AVG ? 1 : 0;
     a.nf = (float)p.nranks;
+    a.inv = (p.nranks & (p.nranks - 1)) == 0 ? 1.0f / (float)p.nranks : 0.0f;
     const dim3 grid(sh.blocks);
 
     if (p.kind == KIND_FUSED_AG || p.kind == KIND_AG_STEP) {
@@ -459,7 +511,7 @@ hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream) {
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
     const size_t nvec = bytes / 16;
     if (nvec == 0) return hipSuccess;
-    const size_t blocks = ceil_div(nvec, (size_t)kThreads * kUnroll);
+    const size_t blocks = ceil_div(nvec, (size_t)kThreads * kCopyUnroll);
     if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), nvec);
