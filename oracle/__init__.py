@@ -21,6 +21,9 @@ the pages; section numbers are each page's own):
                     集合通信", zzmblog.top, sections 两阶段流程 and 通信量推导).
 * ``tree``       -- a message-passing simulation of recursive doubling
                     ("集合通信基础AllReduce、Ring算法与NCCL全解析", section 4.1).
+* ``halving_doubling`` -- recursive-halving ReduceScatter then
+                    recursive-doubling AllGather (the same page's name for
+                    the tree, read as the bandwidth-optimal variant).
 * ``direct``     -- direct references with no messages: exact integer sums,
                     fp64 sums, the ordered fold the ring performs per chunk,
                     the pairwise fold the tree performs.
@@ -41,6 +44,9 @@ from .ring import (
     simulate_ring_reduce_scatter, simulate_ring_allgather,
 )
 from .tree import simulate_tree_allreduce
+from .halving_doubling import (
+    simulate_hd_reduce_scatter, simulate_hd_allgather, simulate_hd_allreduce, hd_fold_at,
+)
 from .direct import (
     exact_int_sum, exact_max, fp64_sum, ordered_ring_fold,
     ring_fold_at, pairwise_tree_fold, tree_fold_at,
@@ -53,5 +59,6 @@ __all__ = [
     "simulate_ring_allreduce", "simulate_ring_reduce_scatter",
     "simulate_ring_allgather", "simulate_tree_allreduce", "exact_int_sum",
     "exact_max", "fp64_sum", "ordered_ring_fold", "ring_fold_at",
-    "pairwise_tree_fold", "tree_fold_at",
+    "pairwise_tree_fold", "tree_fold_at", "simulate_hd_reduce_scatter",
+    "simulate_hd_allgather", "simulate_hd_allreduce", "hd_fold_at",
 ]

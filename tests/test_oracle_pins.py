@@ -459,3 +459,77 @@ def test_planted_mistakes_are_caught(golden, monkeypatch):
     assert not int_pin_holds()
     monkeypatch.setattr(oring, "hop", real_hop)
     assert fold_pin_holds() and avg_pin_holds() and int_pin_holds()
+
+
+# ---------------------------------------------------------------- halving-doubling
+
+def test_hd_order_golden(golden):
+    g = golden("hd_order_n4_fp32.json")
+    xs = [np.array(x, dtype=np.float32) for x in g["inputs"]]
+    expect = np.array(g["expected_every_rank"], dtype=np.float32)
+    tr = oracle.simulate_hd_allreduce(xs, "float32", "sum")
+    for r in range(4):
+        assert (_bits(tr.state[r]) == _bits(expect)).all()
+    assert (_bits(oracle.hd_fold_at(np.stack(xs), "float32", "sum")) == _bits(expect)).all()
+    # recursive doubling pairs differently
+    rd = oracle.simulate_tree_allreduce(xs, "float32", "sum").state[0]
+    assert not (_bits(rd) == _bits(expect)).all()
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16])
+def test_hd_int32_exact_and_invariants(n):
+    for count in (0, 1, n - 1, n, 3 * n + 1, 37, 200):
+        xs = _rand("int32", n, count, seed=n * 13 + count)
+        exact = oracle.exact_int_sum(xs)
+        ar_ = oracle.simulate_hd_allreduce(xs, "int32", "sum")
+        mx = oracle.simulate_hd_allreduce(xs, "int32", "max")
+        for r in range(n):
+            assert (ar_.state[r] == exact).all()
+            assert (mx.state[r] == oracle.exact_max(xs, "int32")).all()
+        assert ar_.steps == 2 * (n.bit_length() - 1)
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_hd_rs_ag_and_direct_fold(n, dtype):
+    for count in (n, 5 * n + 3, 97):
+        xs = _rand(dtype, n, count, seed=count + n)
+        for op in ("sum", "max", "avg"):
+            ar_ = oracle.simulate_hd_allreduce(xs, dtype, op)
+            rs = oracle.simulate_hd_reduce_scatter(xs, dtype, op)
+            ag = oracle.simulate_hd_allgather(rs.state, dtype)
+            direct = oracle.hd_fold_at(np.stack(xs), dtype, op)
+            lay = oracle.chunk_layout(count, n)
+            for r in range(n):
+                lo, ln = lay[r]
+                assert (_bits(rs.state[r][lo:lo + ln]) == _bits(direct[lo:lo + ln])).all()
+                assert (_bits(ag.state[r]) == _bits(ar_.state[r])).all()
+                assert (_bits(ar_.state[r]) == _bits(direct)).all()
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 64])
+def test_hd_traffic_closed_form(n):
+    count = 3 * n
+    xs = _rand("float32", n, count, seed=1)
+    tr = oracle.simulate_hd_allreduce(xs, "float32", "sum")
+    k_bytes = count * 4
+    for r in range(n):
+        assert tr.sent[r] * n == 2 * (n - 1) * k_bytes      # 2(N-1)/N * K, like the ring
+        assert tr.recv[r] == tr.sent[r]
+    for count in (1, n + 1, 7 * n - 3):                      # ragged: the total is still 2(N-1)K
+        xs = _rand("float32", n, count, seed=2)
+        tr = oracle.simulate_hd_allreduce(xs, "float32", "sum")
+        assert sum(tr.sent) == 2 * (n - 1) * count * 4 == sum(tr.recv)
+
+
+def test_hd_fp32_bound_and_broken():
+    xs = _rand("float32", 8, 500, seed=4)
+    tr = oracle.simulate_hd_allreduce(xs, "float32", "sum")
+    ref = np.stack(xs).astype(np.float64).sum(axis=0)
+    absum = np.abs(np.stack(xs).astype(np.float64)).sum(axis=0)
+    u = 2.0 ** -24
+    assert (np.abs(tr.state[0] - ref) <= 3 * u / (1 - 3 * u) * absum).all()   # depth log2 8 = 3
+    with pytest.raises(oracle.BrokenRing):
+        oracle.simulate_hd_allreduce(xs, "float32", "sum", drop=(3, 4))
+    with pytest.raises(ValueError):
+        oracle.simulate_hd_allreduce(xs[:3], "float32", "sum")
