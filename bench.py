@@ -73,7 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=W.DDP_BUCKET.name, choices=sorted(names))
-    ap.add_argument("--algo", default="ring_fused", choices=["ring_fused", "ring_step", "tree"])
+    ap.add_argument("--algo", default="ring_fused",
+                    choices=["ring_fused", "ring_step", "tree", "halving_doubling"])
     ap.add_argument("--sets", type=int, default=0,
                     help="bucket sets to rotate over (0: enough to exceed the Infinity Cache 4x)")
     ap.add_argument("--seed", type=int, default=0)
@@ -170,8 +171,8 @@ def step_bytes(w, algo):
     n, k = w.nranks, w.bytes_per_rank
     if algo == "ring_fused":
         return 2 * n * k                      # N*K read + N*K written
-    if algo == "ring_step":
-        return 5 * (n - 1) * k                # (N-1) x (2K read + K written) + (N-1) x 2K
+    if algo in ("ring_step", "halving_doubling"):
+        return 5 * (n - 1) * k                # ReduceScatter 3(N-1)K + AllGather 2(N-1)K
     return 2 * n * k * (n.bit_length() - 1)   # log2 N steps of 2*N*K
 
 
@@ -191,8 +192,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.algo == "tree" and w.nranks & (w.nranks - 1):
-        print("tree needs a power-of-two rank count", file=sys.stderr)
+    if args.algo in ("tree", "halving_doubling") and w.nranks & (w.nranks - 1):
+        print(f"{args.algo} needs a power-of-two rank count", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     set_bytes = w.nranks * w.bytes_per_rank
@@ -260,7 +261,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "kernel": {"ring_fused": "k_fused", "ring_step": "k_rs_step/k_ag_step",
-                       "tree": "k_tree_step"}[args.algo],
+                       "tree": "k_tree_step",
+                       "halving_doubling": "k_hd_rs_step/k_hd_ag_step"}[args.algo],
             "us_per_launch": round(ms * 1e3, 3),
             "algorithmic_bytes_per_launch": alg_bytes,
         },
@@ -268,8 +270,9 @@ def main():
     }
     if not args.no_others:
         others = {}
-        for algo in ("ring_fused", "ring_step", "tree"):
-            if algo == args.algo or (algo == "tree" and w.nranks & (w.nranks - 1)):
+        for algo in ("ring_fused", "ring_step", "tree", "halving_doubling"):
+            if algo == args.algo or (algo in ("tree", "halving_doubling")
+                                     and w.nranks & (w.nranks - 1)):
                 continue
             reps = max(5, min(args.steps // 4, 100))
             wl, m = time_algo(ar, sets, w, algo, reps, 3)

@@ -45,7 +45,8 @@ typedef struct ar_ctx ar_ctx;
 typedef enum ar_status {
     AR_OK = 0,
     AR_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum, overlap, step index */
-    AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, TREE on non-power-of-two N */
+    AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, TREE / HALVING_DOUBLING on
+                                 non-power-of-two N, TREE on ReduceScatter / AllGather */
     AR_ERR_RUNTIME = 3,       /* the HIP runtime reported an error */
     AR_ERR_NO_MEMORY = 4      /* host allocation of the context failed */
 } ar_status;
@@ -73,12 +74,20 @@ typedef enum ar_op { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
  *                HBM traffic (N*K read + N*K written, K = bytes per rank).
  *  TREE       -- recursive doubling ("集合通信基础AllReduce、Ring算法与NCCL全解析",
  *                xdnf.cn, section 4.1): log2 N steps, partner r XOR 2^s, whole
- *                vectors.  Pairwise fold order.  Power-of-two N only; AllReduce
- *                only. */
+ *                vectors.  Pairwise fold order ((x0+x1)+(x2+x3))...  Power-of-two
+ *                N only; AllReduce only.
+ *  HALVING_DOUBLING -- the same page's "Recursive Doubling / Halving" read as the
+ *                bandwidth-optimal variant: recursive-halving ReduceScatter
+ *                (partners at distance N/2, N/4, ..., 1; rank r ends with chunk
+ *                r) then recursive-doubling AllGather; 2 log2 N steps, (N-1)/N*K
+ *                sent per rank per phase like the ring.  Fold order
+ *                ((x0+x4)+(x2+x6))+((x1+x5)+(x3+x7)) for N = 8.  Power-of-two N
+ *                only; AllReduce, ReduceScatter and AllGather. */
 typedef enum ar_algo {
     AR_ALGO_RING_STEP = 0,
     AR_ALGO_RING_FUSED = 1,
-    AR_ALGO_TREE = 2
+    AR_ALGO_TREE = 2,
+    AR_ALGO_HALVING_DOUBLING = 3
 } ar_algo;
 
 /* Create a context bound to HIP device `device` and stream `stream`
@@ -92,21 +101,23 @@ ar_status ar_create(ar_ctx** out, int device, void* stream);
 ar_status ar_set_stream(ar_ctx* ctx, void* stream);
 
 /* AllReduce in place: every bufs[r][0:count) ends with the reduction of all
- * ranks' inputs.  RING_STEP and RING_FUSED give identical bits; TREE gives
- * the pairwise-order result. */
+ * ranks' inputs.  RING_STEP and RING_FUSED give identical bits; TREE and
+ * HALVING_DOUBLING give their tree-order results. */
 ar_status ar_allreduce(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
                        ar_dtype dtype, ar_op op, ar_algo algo);
 
 /* ReduceScatter in place ("AllReduce 集合通信", zzmblog.top, section 语义: each
  * process ends with one shard of the reduction).  On return bufs[r] holds the
  * finished chunk r at its natural offset (ar_chunk_range(count, nranks, r));
- * the other chunks of bufs[r] are unspecified.  RING_STEP or RING_FUSED. */
+ * the other chunks of bufs[r] are unspecified.  RING_STEP, RING_FUSED or
+ * HALVING_DOUBLING. */
 ar_status ar_reduce_scatter(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
                             ar_dtype dtype, ar_op op, ar_algo algo);
 
 /* AllGather in place: chunk r of bufs[r] is copied, bit for bit, into chunk r
  * of every other buffer.  ar_reduce_scatter then ar_allgather with the same
- * algo equals ar_allreduce bitwise.  RING_STEP or RING_FUSED. */
+ * algo equals ar_allreduce bitwise.  RING_STEP, RING_FUSED or
+ * HALVING_DOUBLING. */
 ar_status ar_allgather(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
                        ar_dtype dtype, ar_algo algo);
 
@@ -127,6 +138,20 @@ ar_status ar_ring_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t cou
  * last step divides by N.  Power-of-two nranks only. */
 ar_status ar_tree_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
                        ar_dtype dtype, ar_op op, int step);
+
+/* One recursive-halving ReduceScatter step s (0 <= s < log2 N): with
+ * d = N >> (s+1), every rank r folds partner (r XOR d)'s copy of the d chunks
+ * starting at (r & ~(d-1)) into its own; with AR_AVG the last step divides
+ * the finished chunk r by N.  Power-of-two nranks only.  Calling s = 0..log2N-1
+ * in order equals ar_reduce_scatter(HALVING_DOUBLING). */
+ar_status ar_hd_rs_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                        ar_dtype dtype, ar_op op, int step);
+
+/* One recursive-doubling AllGather step t (0 <= t < log2 N): with d = 2^t,
+ * every rank r copies the d finished chunks of partner (r XOR d), i.e. chunks
+ * ((r XOR d) & ~(d-1)) ... + d-1.  Power-of-two nranks only. */
+ar_status ar_hd_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                        ar_dtype dtype, int step);
 
 /* Chunk c's element range (host-only; touches no GPU).  Errors: nranks out of
  * range, chunk outside [0, nranks), NULL outputs -> AR_ERR_INVALID_ARG. */

@@ -23,7 +23,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
-    "ring_ag_step", "tree_step", "copy_", "chunk_range", "bind", "context", "LIB_PATH",
+    "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "copy_", "chunk_range", "bind",
+    "context", "LIB_PATH",
 ]
 
 _ctx: dict = {}
@@ -113,6 +114,18 @@ def ring_ag_step(tensors, step: int):
 def tree_step(tensors, op: str, step: int):
     ts, dt, count, dev = _check(tensors)
     context(dev).tree_step_ptrs([t.data_ptr() for t in ts], count, dt, op, step)
+    return ts
+
+
+def hd_rs_step(tensors, op: str, step: int):
+    ts, dt, count, dev = _check(tensors)
+    context(dev).hd_rs_step_ptrs([t.data_ptr() for t in ts], count, dt, op, step)
+    return ts
+
+
+def hd_ag_step(tensors, step: int):
+    ts, dt, count, dev = _check(tensors)
+    context(dev).hd_ag_step_ptrs([t.data_ptr() for t in ts], count, dt, step)
     return ts
 
 

@@ -23,12 +23,13 @@ AR_ERR_NO_MEMORY = 4
 
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {"sum": 0, "max": 1, "avg": 2}
-ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2}
+ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2, "halving_doubling": 3}
 
 # every symbol include/ar.h declares
 EXPORTS = (
     "ar_create", "ar_set_stream", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
-    "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_chunk_range", "ar_copy",
+    "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
+    "ar_chunk_range", "ar_copy",
     "ar_status_string", "ar_last_error", "ar_destroy",
 )
 
@@ -60,6 +61,8 @@ def _load() -> ctypes.CDLL:
         "ar_ring_rs_step": ([vp, pp, i, sz, i, i, i], i),
         "ar_ring_ag_step": ([vp, pp, i, sz, i, i], i),
         "ar_tree_step": ([vp, pp, i, sz, i, i, i], i),
+        "ar_hd_rs_step": ([vp, pp, i, sz, i, i, i], i),
+        "ar_hd_ag_step": ([vp, pp, i, sz, i, i], i),
         "ar_chunk_range": ([sz, i, i, ctypes.POINTER(sz), ctypes.POINTER(sz)], i),
         "ar_copy": ([vp, vp, vp, sz], i),
         "ar_status_string": ([i], cp),
@@ -148,6 +151,16 @@ class Context:
         arr = _ptr_array(ptrs)
         self._check(lib.ar_tree_step(self._h, arr, len(ptrs), count, DTYPES[dtype], OPS[op],
                                      step), "ar_tree_step")
+
+    def hd_rs_step_ptrs(self, ptrs, count, dtype, op, step):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_hd_rs_step(self._h, arr, len(ptrs), count, DTYPES[dtype], OPS[op],
+                                      step), "ar_hd_rs_step")
+
+    def hd_ag_step_ptrs(self, ptrs, count, dtype, step):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_hd_ag_step(self._h, arr, len(ptrs), count, DTYPES[dtype], step),
+                    "ar_hd_ag_step")
 
     def copy_ptrs(self, dst, src, nbytes):
         self._check(lib.ar_copy(self._h, dst, src, nbytes), "ar_copy")

@@ -61,7 +61,13 @@ size_t elem_bytes(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
 bool valid_dtype(int d) { return d == AR_INT32 || d == AR_FLOAT32 || d == AR_BFLOAT16; }
 bool valid_op(int o) { return o == AR_SUM || o == AR_MAX || o == AR_AVG; }
 bool valid_algo(int a) {
-    return a == AR_ALGO_RING_STEP || a == AR_ALGO_RING_FUSED || a == AR_ALGO_TREE;
+    return a == AR_ALGO_RING_STEP || a == AR_ALGO_RING_FUSED || a == AR_ALGO_TREE ||
+           a == AR_ALGO_HALVING_DOUBLING;
+}
+int log2_exact(int n) {
+    int l = 0;
+    while ((1 << l) < n) ++l;
+    return l;
 }
 bool pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
 
@@ -205,8 +211,8 @@ ar_status check_op(ar_ctx* ctx, int dtype, int op) {
 }
 
 ar_status check_shape(ar_ctx* ctx, arlib::Kind k, int dtype, int nranks, size_t count,
-                      bool vec) {
-    arlib::Plan p = make_plan(k, dtype, AR_SUM, nranks, count, 0, vec, 0);
+                      bool vec, int step = 0) {
+    arlib::Plan p = make_plan(k, dtype, AR_SUM, nranks, count, step, vec, 0);
     arlib::Shape sh;
     if (!arlib::plan_shape(p, &sh))
         return fail(ctx, AR_ERR_INVALID_ARG, "count %zu needs more blocks than one grid holds",
@@ -230,18 +236,21 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
         unsigned mis = 0;
         ar_status s = check_buffers(ctx, bufs, nranks, count, dtype, &vec, &mis);
         if (s != AR_OK) return s;
-        if (algo == AR_ALGO_TREE) {
-            if (coll != COLL_AR)
-                return fail(ctx, AR_ERR_UNSUPPORTED,
-                            "TREE is an AllReduce algorithm; use RING_STEP or RING_FUSED");
-            if (!pow2(nranks))
-                return fail(ctx, AR_ERR_UNSUPPORTED,
-                            "TREE (recursive doubling) needs a power-of-two nranks, got %d",
-                            nranks);
-        }
+        if (algo == AR_ALGO_TREE && coll != COLL_AR)
+            return fail(ctx, AR_ERR_UNSUPPORTED,
+                        "TREE is an AllReduce algorithm; use RING_STEP, RING_FUSED or "
+                        "HALVING_DOUBLING");
+        if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING) && !pow2(nranks))
+            return fail(ctx, AR_ERR_UNSUPPORTED,
+                        "%s needs a power-of-two nranks, got %d",
+                        algo == AR_ALGO_TREE ? "TREE (recursive doubling)" : "HALVING_DOUBLING",
+                        nranks);
         if (count == 0 || nranks == 1) return AR_OK;
-        const arlib::Kind probe = algo == AR_ALGO_TREE ? arlib::KIND_TREE_STEP : arlib::KIND_RS_STEP;
-        s = check_shape(ctx, probe, dtype, nranks, count, vec);
+        const arlib::Kind probe = algo == AR_ALGO_TREE ? arlib::KIND_TREE_STEP
+                                  : algo == AR_ALGO_HALVING_DOUBLING ? arlib::KIND_HD_AG_STEP
+                                                                     : arlib::KIND_RS_STEP;
+        s = check_shape(ctx, probe, dtype, nranks, count, vec,
+                        algo == AR_ALGO_HALVING_DOUBLING ? log2_exact(nranks) - 1 : 0);
         if (s != AR_OK) return s;
 
         DeviceGuard g(ctx->device);
@@ -253,6 +262,24 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
                                   : coll == COLL_RS ? arlib::KIND_FUSED_RS
                                                     : arlib::KIND_FUSED_AG;
             return run(ctx, make_plan(k, dtype, o, nranks, count, 0, vec, mis), t);
+        }
+        if (algo == AR_ALGO_HALVING_DOUBLING) {
+            const int levels = log2_exact(nranks);
+            if (coll != COLL_AG) {
+                for (int st = 0; st < levels; ++st) {
+                    s = run(ctx, make_plan(arlib::KIND_HD_RS_STEP, dtype, o, nranks, count, st,
+                                           vec, mis), t);
+                    if (s != AR_OK) return s;
+                }
+            }
+            if (coll != COLL_RS) {
+                for (int st = 0; st < levels; ++st) {
+                    s = run(ctx, make_plan(arlib::KIND_HD_AG_STEP, dtype, o, nranks, count, st,
+                                           vec, mis), t);
+                    if (s != AR_OK) return s;
+                }
+            }
+            return AR_OK;
         }
         if (algo == AR_ALGO_TREE) {
             for (int st = 0; (1 << st) < nranks; ++st) {
@@ -286,7 +313,7 @@ ar_status single_step(ar_ctx* ctx, arlib::Kind kind, void* const* bufs, int nran
                       int dtype, int op, int step) {
     if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
     try {
-        if (kind != arlib::KIND_AG_STEP) {
+        if (kind != arlib::KIND_AG_STEP && kind != arlib::KIND_HD_AG_STEP) {
             const ar_status s = check_op(ctx, dtype, op);
             if (s != AR_OK && valid_dtype(dtype)) return s;
         }
@@ -295,22 +322,21 @@ ar_status single_step(ar_ctx* ctx, arlib::Kind kind, void* const* bufs, int nran
         ar_status s = check_buffers(ctx, bufs, nranks, count, dtype, &vec, &mis);
         if (s != AR_OK) return s;
         int nsteps = nranks - 1;
-        if (kind == arlib::KIND_TREE_STEP) {
+        if (kind == arlib::KIND_TREE_STEP || kind == arlib::KIND_HD_RS_STEP ||
+            kind == arlib::KIND_HD_AG_STEP) {
             if (!pow2(nranks))
                 return fail(ctx, AR_ERR_UNSUPPORTED,
-                            "TREE (recursive doubling) needs a power-of-two nranks, got %d",
-                            nranks);
-            nsteps = 0;
-            while ((1 << nsteps) < nranks) ++nsteps;
+                            "this step needs a power-of-two nranks, got %d", nranks);
+            nsteps = log2_exact(nranks);
         }
         if (step < 0 || step >= nsteps)
             return fail(ctx, AR_ERR_INVALID_ARG, "step %d outside [0, %d)", step, nsteps);
         if (count == 0) return AR_OK;
-        s = check_shape(ctx, kind, dtype, nranks, count, vec);
+        s = check_shape(ctx, kind, dtype, nranks, count, vec, step);
         if (s != AR_OK) return s;
         DeviceGuard g(ctx->device);
         if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
-        const int o = kind == arlib::KIND_AG_STEP ? AR_SUM : op;
+        const int o = (kind == arlib::KIND_AG_STEP || kind == arlib::KIND_HD_AG_STEP) ? AR_SUM : op;
         return run(ctx, make_plan(kind, dtype, o, nranks, count, step, vec, mis),
                    table_of(bufs, nranks));
     } catch (...) {
@@ -375,6 +401,18 @@ ar_status ar_ring_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t cou
 ar_status ar_tree_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
                        ar_op op, int step) {
     return single_step(ctx, arlib::KIND_TREE_STEP, bufs, nranks, count, (int)dtype, (int)op, step);
+}
+
+ar_status ar_hd_rs_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                        ar_dtype dtype, ar_op op, int step) {
+    return single_step(ctx, arlib::KIND_HD_RS_STEP, bufs, nranks, count, (int)dtype, (int)op,
+                       step);
+}
+
+ar_status ar_hd_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                        ar_dtype dtype, int step) {
+    return single_step(ctx, arlib::KIND_HD_AG_STEP, bufs, nranks, count, (int)dtype, AR_SUM,
+                       step);
 }
 
 ar_status ar_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* len) {

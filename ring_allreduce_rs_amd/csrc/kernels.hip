@@ -26,6 +26,10 @@
 //   k_tree_step    one recursive-doubling step ("集合通信基础AllReduce、Ring算法
 //                  与NCCL全解析", section 4.1): both partners of a pair get the
 //                  combination of their vectors.
+//   k_hd_rs_step / k_hd_ag_step
+//                  recursive-halving ReduceScatter and recursive-doubling
+//                  AllGather steps (the same page's "Recursive Doubling /
+//                  Halving", read as the bandwidth-optimal variant).
 //   k_copy         plain 16-byte copy, the bandwidth / counter calibration.
 //
 // Block -> work mapping: block b handles tile (b mod tiles) of chunk
@@ -47,10 +51,10 @@ namespace arlib {
 #endif
 
 #ifndef AR_FUSED_THREADS
-#define AR_FUSED_THREADS 256
+#define AR_FUSED_THREADS 64
 #endif
 #ifndef AR_FUSED_UNROLL
-#define AR_FUSED_UNROLL 2
+#define AR_FUSED_UNROLL 4
 #endif
 #ifndef AR_SPECIALIZE_N
 #define AR_SPECIALIZE_N 1
@@ -370,6 +374,47 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(const Args a) {
                                     fin, a.nf, a.inv);
 }
 
+// Recursive-halving ReduceScatter step s: distance d = N / 2^(s+1); rank r
+// keeps the d chunks starting at r with its low log2(d) bits cleared and folds
+// partner r^d's copy of them into its own.  The partner keeps the other half
+// of the same 2d-chunk segment, so nothing read in a step is written in it.
+// After the last step (d = 1) rank r holds the finished chunk r.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_hd_rs_step(const Args a) {
+    const int n = a.n;
+    const int r = (int)(blockIdx.x / a.tiles);
+    const unsigned tile = blockIdx.x - (unsigned)r * a.tiles;
+    const int d = n >> (a.step + 1);
+    const int keep = r & ~(d - 1);
+    const int p = r ^ d;
+    size_t lo, len0, lo1, len1;
+    chunk_bounds(a, keep, lo, len0);
+    chunk_bounds(a, keep + d - 1, lo1, len1);
+    const size_t len = lo1 + len1 - lo;
+    if (len == 0) return;
+    const bool fin = a.avg && d == 1;
+    pair_range<Op, VEC, true, false>(rank_ptr(a, p), rank_ptr(a, r), lo, len, a.mis, tile, fin,
+                                     a.nf, a.inv);
+}
+
+// Recursive-doubling AllGather step t: distance d = 2^t; rank r copies the d
+// finished chunks held by partner r^d.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_hd_ag_step(const Args a) {
+    const int r = (int)(blockIdx.x / a.tiles);
+    const unsigned tile = blockIdx.x - (unsigned)r * a.tiles;
+    const int d = 1 << a.step;
+    const int p = r ^ d;
+    const int first = p & ~(d - 1);
+    size_t lo, len0, lo1, len1;
+    chunk_bounds(a, first, lo, len0);
+    chunk_bounds(a, first + d - 1, lo1, len1);
+    const size_t len = lo1 + len1 - lo;
+    if (len == 0) return;
+    pair_range<Op, VEC, false, false>(rank_ptr(a, p), rank_ptr(a, r), lo, len, a.mis, tile,
+                                      false, a.nf, a.inv);
+}
+
 __global__ __launch_bounds__(kThreads) void k_copy(u32x4* __restrict__ dst,
                                                    const u32x4* __restrict__ src, size_t nvec) {
     const size_t base = (size_t)blockIdx.x * (kThreads * kCopyUnroll) + threadIdx.x;
@@ -402,6 +447,13 @@ bool plan_shape(const Plan& p, Shape* out) {
     if (p.kind == KIND_TREE_STEP) {
         tiles = ceil_div(ceil_div(p.count, epu), per_tile);
         groups = (size_t)p.nranks / 2;
+    } else if (p.kind == KIND_HD_RS_STEP || p.kind == KIND_HD_AG_STEP) {
+        // a step moves d consecutive chunks per rank
+        const size_t per = ceil_div(p.count, (size_t)p.nranks);
+        const size_t d = p.kind == KIND_HD_RS_STEP ? ((size_t)p.nranks >> (p.step + 1))
+                                                   : ((size_t)1 << p.step);
+        tiles = ceil_div(ceil_div(per * d, epu), per_tile);
+        groups = (size_t)p.nranks;
     } else {
         const size_t per = ceil_div(p.count, (size_t)p.nranks);
         tiles = ceil_div(ceil_div(per, epu), per_tile);
@@ -441,6 +493,9 @@ static hipError_t launch_kind(const Plan& p, const Args& a, dim3 grid, hipStream
         case KIND_TREE_STEP:
             hipLaunchKernelGGL((k_tree_step<Op, VEC>), grid, block, 0, s, a);
             break;
+        case KIND_HD_RS_STEP:
+            hipLaunchKernelGGL((k_hd_rs_step<Op, VEC>), grid, block, 0, s, a);
+            break;
         default:
             return hipErrorInvalidValue;
     }
@@ -458,6 +513,9 @@ static hipError_t launch_copy_kind(const Plan& p, const Args& a, dim3 grid, hipS
             break;
         case KIND_AG_STEP:
             hipLaunchKernelGGL((k_ag_step<Op, VEC>), grid, block, 0, s, a);
+            break;
+        case KIND_HD_AG_STEP:
+            hipLaunchKernelGGL((k_hd_ag_step<Op, VEC>), grid, block, 0, s, a);
             break;
         default:
             return hipErrorInvalidValue;
@@ -486,7 +544,7 @@ hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream) {
     a.inv = (p.nranks & (p.nranks - 1)) == 0 ? 1.0f / (float)p.nranks : 0.0f;
     const dim3 grid(sh.blocks);
 
-    if (p.kind == KIND_FUSED_AG || p.kind == KIND_AG_STEP) {
+    if (p.kind == KIND_FUSED_AG || p.kind == KIND_AG_STEP || p.kind == KIND_HD_AG_STEP) {
         if (elem_bytes(p.dtype) == 2)
             return p.vec ? launch_copy_kind<2, true>(p, a, grid, stream)
                          : launch_copy_kind<2, false>(p, a, grid, stream);

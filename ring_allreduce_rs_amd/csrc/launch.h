@@ -22,6 +22,8 @@ enum Kind {
     KIND_RS_STEP = 3,    // one ReduceScatter step of the ring
     KIND_AG_STEP = 4,    // one AllGather step of the ring
     KIND_TREE_STEP = 5,  // one recursive-doubling step
+    KIND_HD_RS_STEP = 6, // one recursive-halving ReduceScatter step
+    KIND_HD_AG_STEP = 7, // one recursive-doubling AllGather step
 };
 
 struct Plan {

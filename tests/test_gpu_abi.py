@@ -61,6 +61,8 @@ def test_invalid_arguments_are_rejected_before_launch(ctx):
         "rs step negative": lambda: ctx.ring_rs_step_ptrs(p, 64, "float32", "sum", -1),
         "ag step range": lambda: ctx.ring_ag_step_ptrs(p, 64, "float32", 3),
         "tree step range": lambda: ctx.tree_step_ptrs(p, 64, "float32", "sum", 2),
+        "hd rs step range": lambda: ctx.hd_rs_step_ptrs(p, 64, "float32", "sum", 2),
+        "hd ag step range": lambda: ctx.hd_ag_step_ptrs(p, 64, "float32", -1),
     }
     for name, fn in cases.items():
         assert status_of(fn) == INVALID, name
@@ -89,6 +91,12 @@ def test_unsupported_combinations(ctx):
     p4 = [t.data_ptr() for t in t4]
     assert status_of(lambda: ctx.reduce_scatter_ptrs(p4, 64, "float32", "sum", "tree")) == UNSUPPORTED
     assert status_of(lambda: ctx.allgather_ptrs(p4, 64, "float32", "tree")) == UNSUPPORTED
+    for call in (lambda: ctx.allreduce_ptrs(p3, 64, "float32", "sum", "halving_doubling"),
+                 lambda: ctx.reduce_scatter_ptrs(p3, 64, "float32", "sum", "halving_doubling"),
+                 lambda: ctx.allgather_ptrs(p3, 64, "float32", "halving_doubling"),
+                 lambda: ctx.hd_rs_step_ptrs(p3, 64, "float32", "sum", 0),
+                 lambda: ctx.hd_ag_step_ptrs(p3, 64, "float32", 0)):
+        assert status_of(call) == UNSUPPORTED
 
 
 def test_noops(ctx):
@@ -98,7 +106,7 @@ def test_noops(ctx):
     # one rank: AVG over one rank is the identity
     (t,) = bufs(1, count=1001)
     before = t.clone()
-    for algo in ("ring_step", "ring_fused", "tree"):
+    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling"):
         ar.allreduce([t], op="avg", algo=algo)
     torch.cuda.synchronize()
     assert torch.equal(t, before)

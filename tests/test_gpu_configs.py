@@ -88,6 +88,11 @@ def test_ddp_bucket_config_full_oracle():
     run(ts, "avg", "tree")
     assert ranks_identical(ts)
     assert_bits_equal(to_np(ts[0]), tw, "tree")
+    hw = oracle.simulate_hd_allreduce(xs, "float32", "avg").state[0]
+    ts = to_gpu(xs, "float32")
+    run(ts, "avg", "halving_doubling")
+    assert ranks_identical(ts)
+    assert_bits_equal(to_np(ts[0]), hw, "halving_doubling")
 
 
 @pytest.mark.slow
@@ -130,25 +135,30 @@ def test_sweep_config(w):
         a = W.device_inputs(w, seed=0)
         idx = sample_positions(w.count, w.nranks, k=4096, seed=2)
         vals = gather(a, idx)
-    b, c = clone_all(a), clone_all(a)
+    b, c, h = clone_all(a), clone_all(a), clone_all(a)
     run(a, "sum", "ring_step")
     run(b, "sum", "ring_fused")
     run(c, "sum", "tree")
+    run(h, "sum", "halving_doubling")
     for r in range(w.nranks):
         assert torch.equal(a[r], b[r]), f"fused != step on rank {r}"
-    assert ranks_identical(a) and ranks_identical(c)
+    assert ranks_identical(a) and ranks_identical(c) and ranks_identical(h)
     if full:
         assert_bits_equal(to_np(a[0]), oracle.simulate_ring_allreduce(xs, "float32", "sum").state[0],
                           "ring")
         assert_bits_equal(to_np(c[0]), oracle.simulate_tree_allreduce(xs, "float32", "sum").state[0],
                           "tree")
+        assert_bits_equal(to_np(h[0]), oracle.simulate_hd_allreduce(xs, "float32", "sum").state[0],
+                          "halving_doubling")
     else:
         ring_want = oracle.ring_fold_at(vals, chunk_ids(idx, w.count, w.nranks), w.nranks,
                                         "float32", "sum")
         tree_want = oracle.tree_fold_at(vals, "float32", "sum")
+        hd_want = oracle.hd_fold_at(vals, "float32", "sum")
         assert_bits_equal(gather(a[:1], idx)[0], ring_want, "ring sampled")
         assert_bits_equal(gather(c[:1], idx)[0], tree_want, "tree sampled")
-    del a, b, c
+        assert_bits_equal(gather(h[:1], idx)[0], hd_want, "hd sampled")
+    del a, b, c, h
     torch.cuda.empty_cache()
 
 

@@ -100,11 +100,47 @@ def test_every_tree_step_matches_oracle_snapshot(dtype, op, n, count):
 
 
 @pytest.mark.parametrize("dtype,op", DT_OPS)
-@pytest.mark.parametrize("algo", ["ring_step", "ring_fused"])
+@pytest.mark.parametrize("n,count", [(1, 7), (2, 4099), (4, 6), (4, 24581), (8, 65539),
+                                     (16, 33), (16, 40003), (32, 2050)])
+def test_halving_doubling_allreduce_matches_oracle(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n * 17 + count)
+    want = oracle.simulate_hd_allreduce(xs, dtype, op).state
+    ts = to_gpu(xs, dtype)
+    ar.allreduce(ts, op=op, algo="halving_doubling")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), want[r], f"hd {dtype} {op} n={n} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "max")])
+@pytest.mark.parametrize("n,count", [(4, 24581), (8, 1000), (16, 40003), (8, 5)])
+def test_every_hd_step_matches_oracle_snapshot(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=count + 2)
+    snaps = oracle.simulate_hd_allreduce(xs, dtype, op, record=True).snapshots
+    levels = n.bit_length() - 1
+    assert len(snaps) == 2 * levels
+    ts = to_gpu(xs, dtype)
+    for s in range(levels):
+        ar.hd_rs_step(ts, op, s)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), snaps[s][r], f"hd RS step {s} rank {r}")
+    for s in range(levels):
+        ar.hd_ag_step(ts, s)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), snaps[levels + s][r], f"hd AG step {s} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("algo", ["ring_step", "ring_fused", "halving_doubling"])
 @pytest.mark.parametrize("n,count", [(3, 10007), (4, 6), (8, 65539), (16, 40003)])
 def test_reduce_scatter_then_allgather(dtype, op, algo, n, count):
+    if algo == "halving_doubling" and n & (n - 1):
+        pytest.skip("halving-doubling needs a power of two")
     xs = rand_inputs(dtype, n, count, seed=count * 3 + n)
-    direct = oracle.ordered_ring_fold(xs, dtype, op)
+    direct = (oracle.hd_fold_at(np.stack(xs), dtype, op) if algo == "halving_doubling"
+              else oracle.ordered_ring_fold(xs, dtype, op))
     ts = to_gpu(xs, dtype)
     ar.reduce_scatter(ts, op=op, algo=algo)
     torch.cuda.synchronize()
@@ -120,11 +156,13 @@ def test_reduce_scatter_then_allgather(dtype, op, algo, n, count):
 
 
 @pytest.mark.parametrize("dtype", ["int32", "float32", "bfloat16"])
-@pytest.mark.parametrize("n,count", [(3, 10007), (8, 65539), (5, 9)])
+@pytest.mark.parametrize("n,count", [(3, 10007), (8, 65539), (5, 9), (4, 3)])
 def test_allgather_copies_owner_chunks(dtype, n, count):
     xs = rand_inputs(dtype, n, count, seed=n + count)
     want = oracle.simulate_ring_allgather(xs, dtype).state
-    for algo in ("ring_step", "ring_fused"):
+    for algo in ("ring_step", "ring_fused", "halving_doubling"):
+        if algo == "halving_doubling" and n & (n - 1):
+            continue
         ts = to_gpu(xs, dtype)
         ar.allgather(ts, algo=algo)
         torch.cuda.synchronize()
@@ -139,11 +177,14 @@ def test_unaligned_buffers(dtype, op, shift, same_alignment):
     """Buffers that start off a 16-byte boundary: a common misalignment takes
     the vector path with element-wise heads and tails, mixed misalignments the
     element-wise path.  Both must equal the oracle bitwise."""
-    n, count = 5, 12345
+    n, count = 4, 12345
     xs = rand_inputs(dtype, n, count, seed=shift + 17)
-    want = oracle.simulate_ring_allreduce(xs, dtype, op).state
+    wants = {"ring": oracle.simulate_ring_allreduce(xs, dtype, op).state,
+             "tree": oracle.simulate_tree_allreduce(xs, dtype, op).state,
+             "halving_doubling": oracle.simulate_hd_allreduce(xs, dtype, op).state}
     stride = ((count + 64 + 7) // 8) * 8          # a multiple of 16 bytes per row
-    for algo in ("ring_step", "ring_fused"):
+    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling"):
+        want = wants["ring" if algo.startswith("ring") else algo]
         store = torch.zeros(n * stride, dtype=to_gpu(xs[:1], dtype)[0].dtype, device="cuda")
         views = []
         for r in range(n):
