@@ -83,6 +83,10 @@ def parse():
                     help="skip the secondary per-step ring / tree / copy measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every algorithm over the 64-rank message-size sweep, fit the "
+                         "latency/bandwidth model T = a + b*K per algorithm and report the "
+                         "ring/tree crossover (one JSON line per point, then one fit line)")
     a = ap.parse_args()
     return a, names[a.workload]
 
@@ -176,6 +180,56 @@ def step_bytes(w, algo):
     return 2 * n * k * (n.bit_length() - 1)   # log2 N steps of 2*N*K
 
 
+def sweep(args):
+    """64 ranks, fp32 U[-1, 1], SUM, 4 KiB .. 64 MiB per rank: time each
+    algorithm and fit T(K) = a + b*K (the alpha-beta model: a = launches x
+    alpha, b = bytes-per-K / bandwidth)."""
+    import numpy as np
+    import torch
+
+    import ring_allreduce_rs_amd as ar
+    import workloads as W
+    algos = ("ring_step", "tree", "halving_doubling", "ring_fused")
+    launches = {"ring_step": 2 * 63, "tree": 6, "halving_doubling": 12, "ring_fused": 1}
+    rows = {a: [] for a in algos}
+    for w in W.SWEEP:
+        set_bytes = w.nranks * w.bytes_per_rank
+        nsets = max(2, min(16, -(-4 * INFINITY_CACHE_BYTES // set_bytes)))
+        sets = [W.device_inputs(w, seed=s) for s in range(nsets)]
+        steps = max(10, min(200, int(2e9 // max(set_bytes, 1))))
+        for algo in algos:
+            wall, ms = time_algo(ar, sets, w, algo, steps, 5)
+            t = wall / steps
+            rows[algo].append((w.bytes_per_rank, t))
+            print(json.dumps({"sweep": w.name, "algo": algo, "nranks": w.nranks,
+                              "bytes_per_rank": w.bytes_per_rank, "rotating_sets": nsets,
+                              "steps": steps, "us_per_allreduce": round(t * 1e6, 3),
+                              "event_us": round(ms * 1e3, 3),
+                              "GBps_algorithmic": round(2 * set_bytes / t / 1e9, 2),
+                              "GBps_bytes_moved": round(step_bytes(w, algo) / t / 1e9, 2)}),
+                  flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    fit = {}
+    for algo in algos:
+        k = np.array([r[0] for r in rows[algo]], dtype=np.float64)
+        t = np.array([r[1] for r in rows[algo]], dtype=np.float64)
+        b, a = np.polyfit(k, t, 1)
+        fit[algo] = {"a_us": round(a * 1e6, 3), "b_us_per_MiB": round(b * 1e6 * (1 << 20), 4),
+                     "alpha_us_per_launch": round(a * 1e6 / launches[algo], 3),
+                     "launches": launches[algo],
+                     "bytes_moved_GBps": round(step_bytes(W.SWEEP[-1], algo)
+                                               / W.SWEEP[-1].bytes_per_rank / b / 1e9, 1)}
+    cross = {}
+    for x, y in (("ring_step", "tree"), ("halving_doubling", "tree"), ("ring_step", "ring_fused")):
+        ax, bx = fit[x]["a_us"], fit[x]["b_us_per_MiB"]
+        ay, by = fit[y]["a_us"], fit[y]["b_us_per_MiB"]
+        cross[f"{x}_vs_{y}_MiB"] = (round((ay - ax) / (bx - by), 3) if bx != by else None)
+    print(json.dumps({"sweep_fit": fit, "crossover_bytes_per_rank": cross,
+                      "model": "T(K) = a + b*K fitted over the five sizes; a / launches = alpha"}),
+          flush=True)
+
+
 def main():
     args, w = parse()
     if args.gpus != 1:
@@ -183,6 +237,8 @@ def main():
               f"--gpus {args.gpus} is not a configuration of this path (use --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        return sweep(args)
     import numpy as np
     import torch
 

@@ -28,6 +28,10 @@
  *  - No C++ exception crosses this interface.  A context is not thread-safe;
  *    use one per host thread / stream.
  *  - ar_last_error(ctx) describes the most recent failure on that context.
+ *  - The device-memory check of bufs (device, type, extent inside the
+ *    allocation) is cached per context for the 32 most recent pointer sets;
+ *    a buffer freed and re-allocated smaller at the same address between two
+ *    calls is not re-checked.
  */
 #ifndef RING_ALLREDUCE_AR_H
 #define RING_ALLREDUCE_AR_H
@@ -82,12 +86,19 @@ typedef enum ar_op { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
  *                r) then recursive-doubling AllGather; 2 log2 N steps, (N-1)/N*K
  *                sent per rank per phase like the ring.  Fold order
  *                ((x0+x4)+(x2+x6))+((x1+x5)+(x3+x7)) for N = 8.  Power-of-two N
- *                only; AllReduce, ReduceScatter and AllGather. */
+ *                only; AllReduce, ReduceScatter and AllGather.
+ *  AUTO       -- pick the algorithm with the smallest predicted time under the
+ *                latency/bandwidth model of ar_predict_us (the pages' size-based
+ *                choice between ring and tree: "AllReduce", compassingai.com,
+ *                sections 4-5; xdnf.cn page, section 4.3).  On one GPU the fused
+ *                pass needs one launch and the fewest bytes, so the model picks
+ *                RING_FUSED at every size measured. */
 typedef enum ar_algo {
     AR_ALGO_RING_STEP = 0,
     AR_ALGO_RING_FUSED = 1,
     AR_ALGO_TREE = 2,
-    AR_ALGO_HALVING_DOUBLING = 3
+    AR_ALGO_HALVING_DOUBLING = 3,
+    AR_ALGO_AUTO = 4
 } ar_algo;
 
 /* Create a context bound to HIP device `device` and stream `stream`
@@ -156,6 +167,20 @@ ar_status ar_hd_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
 /* Chunk c's element range (host-only; touches no GPU).  Errors: nranks out of
  * range, chunk outside [0, nranks), NULL outputs -> AR_ERR_INVALID_ARG. */
 ar_status ar_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* len);
+
+/* Predicted time in microseconds of one ar_allreduce with `algo` (not AUTO),
+ * from the alpha-beta model T = t_call + launches * alpha + bytes / BW(algo):
+ * the pages' T_ring ~ 2(N-1) alpha + ... D beta and T_tree ~ 2 log2 N alpha +
+ * ... ("AllReduce", compassingai.com, section 4) with one-GPU launches and HBM
+ * bytes in place of link messages.  Constants were fitted on MI355X over the
+ * 64-rank message-size sweep (host-only; touches no GPU).  Errors: bad
+ * algo / nranks / dtype, NULL us, TREE or HALVING_DOUBLING with a
+ * non-power-of-two nranks -> AR_ERR_INVALID_ARG / AR_ERR_UNSUPPORTED. */
+ar_status ar_predict_us(ar_algo algo, int nranks, size_t count, ar_dtype dtype, double* us);
+
+/* The algorithm AR_ALGO_AUTO resolves to for an AllReduce of this shape
+ * (host-only). */
+ar_status ar_auto_algo(int nranks, size_t count, ar_dtype dtype, ar_algo* out);
 
 /* Plain device-to-device copy of `bytes` bytes (16-byte aligned pointers and
  * size), used to calibrate bandwidth and hardware byte counters against a

@@ -18,13 +18,14 @@ from __future__ import annotations
 import ctypes
 
 from ._lib import (  # noqa: F401
-    ALGOS, AR_MAX_RANKS, DTYPES, EXPORTS, LIB_PATH, OPS, ArError, Context, chunk_range, lib,
+    ALGOS, AR_MAX_RANKS, DTYPES, EXPORTS, LIB_PATH, OPS, ArError, Context, auto_algo,
+    chunk_range, lib, predict_us,
 )
 
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
     "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "copy_", "chunk_range", "bind",
-    "context", "LIB_PATH",
+    "context", "LIB_PATH", "predict_us", "auto_algo",
 ]
 
 _ctx: dict = {}

@@ -23,13 +23,14 @@ AR_ERR_NO_MEMORY = 4
 
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {"sum": 0, "max": 1, "avg": 2}
-ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2, "halving_doubling": 3}
+ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2, "halving_doubling": 3, "auto": 4}
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 # every symbol include/ar.h declares
 EXPORTS = (
     "ar_create", "ar_set_stream", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
     "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
-    "ar_chunk_range", "ar_copy",
+    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy",
     "ar_status_string", "ar_last_error", "ar_destroy",
 )
 
@@ -45,6 +46,13 @@ class ArError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (SONAME libamdhip64.so.7).  Loading torch
+    # first makes libar.so bind to that same runtime instead of pulling in a
+    # second one from /opt/rocm, which would fail to open the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python ring_allreduce_rs_amd/_build.py` "
@@ -64,6 +72,8 @@ def _load() -> ctypes.CDLL:
         "ar_hd_rs_step": ([vp, pp, i, sz, i, i, i], i),
         "ar_hd_ag_step": ([vp, pp, i, sz, i, i], i),
         "ar_chunk_range": ([sz, i, i, ctypes.POINTER(sz), ctypes.POINTER(sz)], i),
+        "ar_predict_us": ([i, i, sz, i, ctypes.POINTER(ctypes.c_double)], i),
+        "ar_auto_algo": ([i, sz, i, ctypes.POINTER(i)], i),
         "ar_copy": ([vp, vp, vp, sz], i),
         "ar_status_string": ([i], cp),
         "ar_last_error": ([vp], cp),
@@ -90,6 +100,24 @@ def chunk_range(count: int, nranks: int, chunk: int) -> tuple[int, int]:
     if st != AR_OK:
         raise ArError(st, "ar_chunk_range", f"count={count} nranks={nranks} chunk={chunk}")
     return off.value, ln.value
+
+
+def predict_us(algo: str, nranks: int, count: int, dtype: str) -> float:
+    """The library's alpha-beta model time for one AllReduce (host-only)."""
+    out = ctypes.c_double()
+    st = lib.ar_predict_us(ALGOS[algo], nranks, count, DTYPES[dtype], ctypes.byref(out))
+    if st != AR_OK:
+        raise ArError(st, "ar_predict_us", f"{algo} nranks={nranks} count={count}")
+    return out.value
+
+
+def auto_algo(nranks: int, count: int, dtype: str) -> str:
+    """The algorithm AR_ALGO_AUTO picks for this AllReduce shape (host-only)."""
+    out = ctypes.c_int()
+    st = lib.ar_auto_algo(nranks, count, DTYPES[dtype], ctypes.byref(out))
+    if st != AR_OK:
+        raise ArError(st, "ar_auto_algo", f"nranks={nranks} count={count}")
+    return ALGO_NAMES[out.value]
 
 
 class Context:

@@ -23,14 +23,26 @@
 #include "ar.h"
 #include "launch.h"
 
+// A pointer set that passed the device-memory checks, with the byte size it
+// was checked for.
+struct CheckedSet {
+    std::vector<uintptr_t> ptrs;
+    size_t bytes = 0;
+    uint64_t stamp = 0;
+};
+
 struct ar_ctx {
     int device = 0;
     hipStream_t stream = nullptr;
     std::string last_error;
-    // the last pointer set that passed the device-memory checks
-    std::vector<uintptr_t> checked;
-    size_t checked_bytes = 0;
+    // Recently validated pointer sets (least recently used is replaced): a
+    // training loop reduces the same few buckets every step, and checking 64
+    // pointers with the runtime costs more than a small message's kernel.
+    std::vector<CheckedSet> checked;
+    uint64_t clock = 0;
 };
+
+static constexpr size_t kCheckedSets = 32;
 
 namespace {
 
@@ -62,7 +74,7 @@ bool valid_dtype(int d) { return d == AR_INT32 || d == AR_FLOAT32 || d == AR_BFL
 bool valid_op(int o) { return o == AR_SUM || o == AR_MAX || o == AR_AVG; }
 bool valid_algo(int a) {
     return a == AR_ALGO_RING_STEP || a == AR_ALGO_RING_FUSED || a == AR_ALGO_TREE ||
-           a == AR_ALGO_HALVING_DOUBLING;
+           a == AR_ALGO_HALVING_DOUBLING || a == AR_ALGO_AUTO;
 }
 int log2_exact(int n) {
     int l = 0;
@@ -89,6 +101,63 @@ struct DeviceGuard {
             (void)hipSetDevice(prev);
     }
 };
+
+// ---------------------------------------------------------------- cost model
+//
+// T = t_call + launches * alpha + bytes / BW.  Fitted on MI355X (8 and 64
+// ranks, fp32, 4 KiB .. 64 MiB per rank, inputs cold in HBM for >= 1 MiB):
+//   t_call   host validation + first dispatch of a call
+//   alpha    each further dependent launch (the per-step kernels wait for the
+//            previous step)
+//   BW       bytes-moved rate of each kernel family; the per-step kernels
+//            re-read what the previous step wrote, partly from the Infinity
+//            Cache, so their rate can exceed a cold stream's; the fused pass
+//            slows as the number of concurrently written rank buffers grows.
+constexpr double kCallUs = 8.0;
+constexpr double kLaunchUs = 3.4;
+constexpr double kStepGBps = 6000.0;
+constexpr double kTreeGBps = 5400.0;
+
+double fused_gbps(int n) { return n <= 8 ? 5500.0 : n <= 16 ? 4950.0 : 4650.0; }
+
+int log2_ceil(int n) {
+    int l = 0;
+    while ((1 << l) < n) ++l;
+    return l;
+}
+
+double predict_allreduce_us(int algo, int n, size_t count, size_t eb) {
+    const double k = (double)count * (double)eb;   // bytes per rank
+    if (n == 1 || count == 0) return kCallUs;
+    switch (algo) {
+        case AR_ALGO_RING_FUSED:
+            return kCallUs + 2.0 * n * k / (fused_gbps(n) * 1e3);
+        case AR_ALGO_RING_STEP:
+            return kCallUs + (2.0 * (n - 1) - 1) * kLaunchUs + 5.0 * (n - 1) * k / (kStepGBps * 1e3);
+        case AR_ALGO_HALVING_DOUBLING:
+            return kCallUs + (2.0 * log2_ceil(n) - 1) * kLaunchUs +
+                   5.0 * (n - 1) * k / (kStepGBps * 1e3);
+        case AR_ALGO_TREE:
+            return kCallUs + (log2_ceil(n) - 1) * kLaunchUs +
+                   2.0 * n * k * log2_ceil(n) / (kTreeGBps * 1e3);
+    }
+    return 1e300;
+}
+
+int auto_algo(int n, size_t count, size_t eb) {
+    int best = AR_ALGO_RING_FUSED;
+    double best_us = predict_allreduce_us(best, n, count, eb);
+    const int cands[] = {AR_ALGO_RING_STEP, AR_ALGO_HALVING_DOUBLING, AR_ALGO_TREE};
+    for (int a : cands) {
+        if ((a == AR_ALGO_TREE || a == AR_ALGO_HALVING_DOUBLING) && !pow2(n)) continue;
+        const double t = predict_allreduce_us(a, n, count, eb);
+        if (t < best_us) {
+            best_us = t;
+            best = a;
+        }
+    }
+    return best;
+}
 
 // Validates everything that can be checked without touching the data.  On
 // success *vec and *mis describe the common 16-byte alignment of the buffers.
@@ -127,11 +196,17 @@ ar_status check_buffers(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
     *mis = *vec ? m0 : 0;
 
     // Device-memory checks: every buffer must be device memory of ctx->device
-    // and lie inside its allocation.  The last passing set is cached.
-    bool same = ctx->checked.size() == (size_t)nranks && bytes <= ctx->checked_bytes;
-    for (int r = 0; same && r < nranks; ++r)
-        same = ctx->checked[(size_t)r] == reinterpret_cast<uintptr_t>(bufs[r]);
-    if (same) return AR_OK;
+    // and lie inside its allocation.  Passing sets are cached (see ar_ctx).
+    for (CheckedSet& cs : ctx->checked) {
+        if (cs.ptrs.size() != (size_t)nranks || bytes > cs.bytes) continue;
+        bool same = true;
+        for (int r = 0; same && r < nranks; ++r)
+            same = cs.ptrs[(size_t)r] == reinterpret_cast<uintptr_t>(bufs[r]);
+        if (same) {
+            cs.stamp = ++ctx->clock;
+            return AR_OK;
+        }
+    }
     for (int r = 0; r < nranks; ++r) {
         hipPointerAttribute_t at;
         std::memset(&at, 0, sizeof at);
@@ -158,9 +233,19 @@ ar_status check_buffers(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
             return fail(ctx, AR_ERR_INVALID_ARG,
                         "bufs[%d]: %zu bytes run past the end of its allocation", r, bytes);
     }
-    ctx->checked.assign((size_t)nranks, 0);
-    for (int r = 0; r < nranks; ++r) ctx->checked[(size_t)r] = reinterpret_cast<uintptr_t>(bufs[r]);
-    ctx->checked_bytes = bytes;
+    CheckedSet entry;
+    entry.ptrs.resize((size_t)nranks);
+    for (int r = 0; r < nranks; ++r) entry.ptrs[(size_t)r] = reinterpret_cast<uintptr_t>(bufs[r]);
+    entry.bytes = bytes;
+    entry.stamp = ++ctx->clock;
+    if (ctx->checked.size() < kCheckedSets) {
+        ctx->checked.push_back(std::move(entry));
+    } else {
+        size_t oldest = 0;
+        for (size_t i = 1; i < ctx->checked.size(); ++i)
+            if (ctx->checked[i].stamp < ctx->checked[oldest].stamp) oldest = i;
+        ctx->checked[oldest] = std::move(entry);
+    }
     return AR_OK;
 }
 
@@ -236,6 +321,12 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
         unsigned mis = 0;
         ar_status s = check_buffers(ctx, bufs, nranks, count, dtype, &vec, &mis);
         if (s != AR_OK) return s;
+        if (algo == AR_ALGO_AUTO) {
+            // ReduceScatter / AllGather alone follow the AllReduce choice, minus TREE
+            algo = auto_algo(nranks, count, elem_bytes((ar_dtype)dtype));
+            if (algo == AR_ALGO_TREE && coll != COLL_AR) algo = AR_ALGO_RING_FUSED;
+            if (debug_enabled()) std::fprintf(stderr, "[ar] AUTO -> algo %d\n", algo);
+        }
         if (algo == AR_ALGO_TREE && coll != COLL_AR)
             return fail(ctx, AR_ERR_UNSUPPORTED,
                         "TREE is an AllReduce algorithm; use RING_STEP, RING_FUSED or "
@@ -413,6 +504,23 @@ ar_status ar_hd_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
                         ar_dtype dtype, int step) {
     return single_step(ctx, arlib::KIND_HD_AG_STEP, bufs, nranks, count, (int)dtype, AR_SUM,
                        step);
+}
+
+ar_status ar_predict_us(ar_algo algo, int nranks, size_t count, ar_dtype dtype, double* us) {
+    if (!us || nranks < 1 || nranks > AR_MAX_RANKS || !valid_dtype((int)dtype) ||
+        !valid_algo((int)algo) || algo == AR_ALGO_AUTO)
+        return AR_ERR_INVALID_ARG;
+    if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING) && !pow2(nranks))
+        return AR_ERR_UNSUPPORTED;
+    *us = predict_allreduce_us((int)algo, nranks, count, elem_bytes(dtype));
+    return AR_OK;
+}
+
+ar_status ar_auto_algo(int nranks, size_t count, ar_dtype dtype, ar_algo* out) {
+    if (!out || nranks < 1 || nranks > AR_MAX_RANKS || !valid_dtype((int)dtype))
+        return AR_ERR_INVALID_ARG;
+    *out = (ar_algo)auto_algo(nranks, count, elem_bytes(dtype));
+    return AR_OK;
 }
 
 ar_status ar_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* len) {

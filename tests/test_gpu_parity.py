@@ -216,3 +216,27 @@ def test_sides_are_not_shared_state():
     s.synchronize()
     for r in range(4):
         assert_bits_equal(to_np(ts[r]), want[r], "side stream")
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "max")])
+@pytest.mark.parametrize("n,count", [(3, 10007), (8, 65539), (16, 33)])
+def test_auto_runs_the_model_choice(dtype, op, n, count):
+    """AUTO gives exactly the bits of the algorithm the model picks."""
+    xs = rand_inputs(dtype, n, count, seed=count + 5)
+    pick = ar.auto_algo(n, count, dtype)
+    sim = {"ring_fused": oracle.simulate_ring_allreduce, "ring_step": oracle.simulate_ring_allreduce,
+           "tree": oracle.simulate_tree_allreduce,
+           "halving_doubling": oracle.simulate_hd_allreduce}[pick]
+    want = sim(xs, dtype, op).state
+    ts = to_gpu(xs, dtype)
+    ar.allreduce(ts, op=op, algo="auto")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), want[r], f"auto ({pick}) rank {r}")
+    rs = to_gpu(xs, dtype)
+    ar.reduce_scatter(rs, op=op, algo="auto")
+    ar.allgather(rs, algo="auto")
+    torch.cuda.synchronize()
+    if pick != "tree":
+        for r in range(n):
+            assert_bits_equal(to_np(rs[r]), want[r], f"auto RS+AG rank {r}")
