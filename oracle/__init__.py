@@ -24,6 +24,9 @@ the pages; section numbers are each page's own):
 * ``halving_doubling`` -- recursive-halving ReduceScatter then
                     recursive-doubling AllGather (the same page's name for
                     the tree, read as the bandwidth-optimal variant).
+* ``double_tree`` -- two complementary in-order binary trees, each reducing
+                    half of the vector up to its root and broadcasting it
+                    down ("AllReduce", compassingai.com, section 3).
 * ``direct``     -- direct references with no messages: exact integer sums,
                     fp64 sums, the ordered fold the ring performs per chunk,
                     the pairwise fold the tree performs.
@@ -47,6 +50,9 @@ from .tree import simulate_tree_allreduce
 from .halving_doubling import (
     simulate_hd_reduce_scatter, simulate_hd_allgather, simulate_hd_allreduce, hd_fold_at,
 )
+from .double_tree import (
+    simulate_double_tree_allreduce, dtree_fold_at, double_tree_fold,
+)
 from .direct import (
     exact_int_sum, exact_max, fp64_sum, ordered_ring_fold,
     ring_fold_at, pairwise_tree_fold, tree_fold_at,
@@ -61,4 +67,5 @@ __all__ = [
     "exact_max", "fp64_sum", "ordered_ring_fold", "ring_fold_at",
     "pairwise_tree_fold", "tree_fold_at", "simulate_hd_reduce_scatter",
     "simulate_hd_allgather", "simulate_hd_allreduce", "hd_fold_at",
+    "simulate_double_tree_allreduce", "dtree_fold_at", "double_tree_fold",
 ]

@@ -533,3 +533,79 @@ def test_hd_fp32_bound_and_broken():
         oracle.simulate_hd_allreduce(xs, "float32", "sum", drop=(3, 4))
     with pytest.raises(ValueError):
         oracle.simulate_hd_allreduce(xs[:3], "float32", "sum")
+
+
+# ---------------------------------------------------------------- double binary tree
+
+def test_dtree_shape_is_complementary():
+    from oracle.double_tree import children, rank_at
+    for n in (2, 4, 8, 16, 64):
+        for t in (0, 1):
+            seen = [rank_at(t, 0, n)]
+            stack = [0]
+            while stack:                                   # every position reached once
+                v = stack.pop()
+                for c in children(v, n):
+                    seen.append(rank_at(t, c, n))
+                    stack.append(c)
+            assert sorted(seen) == list(range(n))
+        if n >= 4:
+            leaves = [{rank_at(t, v, n) for v in range(1, n) if not children(v, n)} for t in (0, 1)]
+            interior = [set(range(n)) - lv for lv in leaves]
+            assert leaves[0] <= interior[1] and leaves[1] <= interior[0]
+
+
+def test_dtree_order_golden(golden):
+    g = golden("dtree_order_n4_fp32.json")
+    xs = [np.array(x, dtype=np.float32) for x in g["inputs"]]
+    expect = np.array(g["expected_every_rank"], dtype=np.float32)
+    tr = oracle.simulate_double_tree_allreduce(xs, "float32", "sum")
+    for r in range(4):
+        assert (_bits(tr.state[r]) == _bits(expect)).all()
+    assert (_bits(oracle.double_tree_fold(xs, "float32", "sum")) == _bits(expect)).all()
+    rd = oracle.simulate_tree_allreduce(xs, "float32", "sum").state[0]
+    assert not (_bits(rd) == _bits(expect)).all()
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16])
+def test_dtree_int32_exact_and_steps(n):
+    for count in (0, 1, 2, n, 3 * n + 1, 37, 200):
+        xs = _rand("int32", n, count, seed=n * 7 + count)
+        tr = oracle.simulate_double_tree_allreduce(xs, "int32", "sum")
+        mx = oracle.simulate_double_tree_allreduce(xs, "int32", "max")
+        for r in range(n):
+            assert (tr.state[r] == oracle.exact_int_sum(xs)).all()
+            assert (mx.state[r] == oracle.exact_max(xs, "int32")).all()
+        assert tr.steps == 2 * (n.bit_length() - 1)
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_dtree_matches_direct_fold(n, dtype):
+    for count in (1, n + 3, 101):
+        xs = _rand(dtype, n, count, seed=count * n)
+        for op in ("sum", "max", "avg"):
+            tr = oracle.simulate_double_tree_allreduce(xs, dtype, op)
+            ref = oracle.double_tree_fold(xs, dtype, op)
+            for r in range(n):
+                assert (_bits(tr.state[r]) == _bits(ref)).all()
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 64])
+def test_dtree_traffic_closed_form(n):
+    from oracle.double_tree import children, rank_at
+    count = 2 * n + 1                                   # halves of n+1 and n elements
+    xs = _rand("float32", n, count, seed=3)
+    tr = oracle.simulate_double_tree_allreduce(xs, "float32", "sum")
+    halves = [(n + 1) * 4, n * 4]
+    # per tree: N-1 partials go up and N-1 results come down
+    assert sum(tr.sent) == sum(tr.recv) == 2 * (n - 1) * sum(halves)
+    for r in range(n):
+        want = 0
+        for t in (0, 1):
+            v = [p for p in range(n) if rank_at(t, p, n) == r][0]
+            # up: a non-root sends its partial once; down: one copy per child
+            want += ((v != 0) + len(children(v, n))) * halves[t]
+        assert tr.sent[r] == want == tr.recv[r]
+    with pytest.raises(oracle.BrokenRing):
+        oracle.simulate_double_tree_allreduce(xs, "float32", "sum", drop=(1, 0))
