@@ -74,7 +74,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=W.DDP_BUCKET.name, choices=sorted(names))
     ap.add_argument("--algo", default="ring_fused",
-                    choices=["ring_fused", "ring_step", "tree", "halving_doubling"])
+                    choices=["ring_fused", "ring_step", "tree", "halving_doubling",
+                             "double_tree"])
     ap.add_argument("--sets", type=int, default=0,
                     help="bucket sets to rotate over (0: enough to exceed the Infinity Cache 4x)")
     ap.add_argument("--seed", type=int, default=0)
@@ -177,6 +178,8 @@ def step_bytes(w, algo):
         return 2 * n * k                      # N*K read + N*K written
     if algo in ("ring_step", "halving_doubling"):
         return 5 * (n - 1) * k                # ReduceScatter 3(N-1)K + AllGather 2(N-1)K
+    if algo == "double_tree":
+        return (7 * (n // 2 - 1) + 5) * k     # two trees, each over half the vector
     return 2 * n * k * (n.bit_length() - 1)   # log2 N steps of 2*N*K
 
 
@@ -189,8 +192,9 @@ def sweep(args):
 
     import ring_allreduce_rs_amd as ar
     import workloads as W
-    algos = ("ring_step", "tree", "halving_doubling", "ring_fused")
-    launches = {"ring_step": 2 * 63, "tree": 6, "halving_doubling": 12, "ring_fused": 1}
+    algos = ("ring_step", "tree", "halving_doubling", "double_tree", "ring_fused")
+    launches = {"ring_step": 2 * 63, "tree": 6, "halving_doubling": 12, "double_tree": 12,
+                "ring_fused": 1}
     rows = {a: [] for a in algos}
     for w in W.SWEEP:
         set_bytes = w.nranks * w.bytes_per_rank
@@ -248,7 +252,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.algo in ("tree", "halving_doubling") and w.nranks & (w.nranks - 1):
+    if args.algo in ("tree", "halving_doubling", "double_tree") and w.nranks & (w.nranks - 1):
         print(f"{args.algo} needs a power-of-two rank count", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
@@ -318,7 +322,8 @@ def main():
             "traffic": traffic,
             "kernel": {"ring_fused": "k_fused", "ring_step": "k_rs_step/k_ag_step",
                        "tree": "k_tree_step",
-                       "halving_doubling": "k_hd_rs_step/k_hd_ag_step"}[args.algo],
+                       "halving_doubling": "k_hd_rs_step/k_hd_ag_step",
+                       "double_tree": "k_dtree_step"}[args.algo],
             "us_per_launch": round(ms * 1e3, 3),
             "algorithmic_bytes_per_launch": alg_bytes,
         },
@@ -326,8 +331,8 @@ def main():
     }
     if not args.no_others:
         others = {}
-        for algo in ("ring_fused", "ring_step", "tree", "halving_doubling"):
-            if algo == args.algo or (algo in ("tree", "halving_doubling")
+        for algo in ("ring_fused", "ring_step", "tree", "halving_doubling", "double_tree"):
+            if algo == args.algo or (algo in ("tree", "halving_doubling", "double_tree")
                                      and w.nranks & (w.nranks - 1)):
                 continue
             reps = max(5, min(args.steps // 4, 100))

@@ -49,8 +49,9 @@ typedef struct ar_ctx ar_ctx;
 typedef enum ar_status {
     AR_OK = 0,
     AR_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum, overlap, step index */
-    AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, TREE / HALVING_DOUBLING on
-                                 non-power-of-two N, TREE on ReduceScatter / AllGather */
+    AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, TREE / HALVING_DOUBLING /
+                                 DOUBLE_TREE on non-power-of-two N, TREE / DOUBLE_TREE on
+                                 ReduceScatter / AllGather */
     AR_ERR_RUNTIME = 3,       /* the HIP runtime reported an error */
     AR_ERR_NO_MEMORY = 4      /* host allocation of the context failed */
 } ar_status;
@@ -87,6 +88,16 @@ typedef enum ar_op { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
  *                sent per rank per phase like the ring.  Fold order
  *                ((x0+x4)+(x2+x6))+((x1+x5)+(x3+x7)) for N = 8.  Power-of-two N
  *                only; AllReduce, ReduceScatter and AllGather.
+ *  DOUBLE_TREE -- two complementary binary trees, each reducing half of the
+ *                vector from the leaves to its root and broadcasting it back
+ *                ("AllReduce", compassingai.com, section 3).  In-order shape:
+ *                position 0 is the root with the single child N/2; position v
+ *                with lowest set bit b > 1 has children v - b/2 and v + b/2.
+ *                Tree 0 places rank v at position v and carries elements
+ *                [0, ceil(count/2)); tree 1 places rank (v-1) mod N at position
+ *                v and carries the rest.  A node folds (left + own) + right;
+ *                the root folds own + child.  2 log2 N steps; power-of-two N;
+ *                AllReduce only.
  *  AUTO       -- pick the algorithm with the smallest predicted time under the
  *                latency/bandwidth model of ar_predict_us (the pages' size-based
  *                choice between ring and tree: "AllReduce", compassingai.com,
@@ -98,7 +109,8 @@ typedef enum ar_algo {
     AR_ALGO_RING_FUSED = 1,
     AR_ALGO_TREE = 2,
     AR_ALGO_HALVING_DOUBLING = 3,
-    AR_ALGO_AUTO = 4
+    AR_ALGO_AUTO = 4,
+    AR_ALGO_DOUBLE_TREE = 5
 } ar_algo;
 
 /* Create a context bound to HIP device `device` and stream `stream`
@@ -163,6 +175,14 @@ ar_status ar_hd_rs_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
  * ((r XOR d) & ~(d-1)) ... + d-1.  Power-of-two nranks only. */
 ar_status ar_hd_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
                         ar_dtype dtype, int step);
+
+/* One double-binary-tree step s (0 <= s < 2 log2 N), both trees at once:
+ * s < L-1 reduces tree level s+1, s = L-1 folds the roots (AVG divides
+ * there), s = L copies each root to position N/2, s > L broadcasts level
+ * 2L-s to its children (L = log2 N).  Power-of-two nranks only.  Calling
+ * s = 0..2L-1 in order equals ar_allreduce(DOUBLE_TREE). */
+ar_status ar_dtree_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                        ar_dtype dtype, ar_op op, int step);
 
 /* Chunk c's element range (host-only; touches no GPU).  Errors: nranks out of
  * range, chunk outside [0, nranks), NULL outputs -> AR_ERR_INVALID_ARG. */

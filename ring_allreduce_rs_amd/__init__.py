@@ -24,7 +24,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
-    "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "copy_", "chunk_range", "bind",
+    "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "dtree_step", "copy_", "chunk_range", "bind",
     "context", "LIB_PATH", "predict_us", "auto_algo",
 ]
 
@@ -127,6 +127,12 @@ def hd_rs_step(tensors, op: str, step: int):
 def hd_ag_step(tensors, step: int):
     ts, dt, count, dev = _check(tensors)
     context(dev).hd_ag_step_ptrs([t.data_ptr() for t in ts], count, dt, step)
+    return ts
+
+
+def dtree_step(tensors, op: str, step: int):
+    ts, dt, count, dev = _check(tensors)
+    context(dev).dtree_step_ptrs([t.data_ptr() for t in ts], count, dt, op, step)
     return ts
 
 

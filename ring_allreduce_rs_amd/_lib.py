@@ -23,13 +23,15 @@ AR_ERR_NO_MEMORY = 4
 
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {"sum": 0, "max": 1, "avg": 2}
-ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2, "halving_doubling": 3, "auto": 4}
+ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2, "halving_doubling": 3, "auto": 4,
+         "double_tree": 5}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 # every symbol include/ar.h declares
 EXPORTS = (
     "ar_create", "ar_set_stream", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
     "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
+    "ar_dtree_step",
     "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy",
     "ar_status_string", "ar_last_error", "ar_destroy",
 )
@@ -71,6 +73,7 @@ def _load() -> ctypes.CDLL:
         "ar_tree_step": ([vp, pp, i, sz, i, i, i], i),
         "ar_hd_rs_step": ([vp, pp, i, sz, i, i, i], i),
         "ar_hd_ag_step": ([vp, pp, i, sz, i, i], i),
+        "ar_dtree_step": ([vp, pp, i, sz, i, i, i], i),
         "ar_chunk_range": ([sz, i, i, ctypes.POINTER(sz), ctypes.POINTER(sz)], i),
         "ar_predict_us": ([i, i, sz, i, ctypes.POINTER(ctypes.c_double)], i),
         "ar_auto_algo": ([i, sz, i, ctypes.POINTER(i)], i),
@@ -189,6 +192,11 @@ class Context:
         arr = _ptr_array(ptrs)
         self._check(lib.ar_hd_ag_step(self._h, arr, len(ptrs), count, DTYPES[dtype], step),
                     "ar_hd_ag_step")
+
+    def dtree_step_ptrs(self, ptrs, count, dtype, op, step):
+        arr = _ptr_array(ptrs)
+        self._check(lib.ar_dtree_step(self._h, arr, len(ptrs), count, DTYPES[dtype], OPS[op],
+                                      step), "ar_dtree_step")
 
     def copy_ptrs(self, dst, src, nbytes):
         self._check(lib.ar_copy(self._h, dst, src, nbytes), "ar_copy")

@@ -74,7 +74,7 @@ bool valid_dtype(int d) { return d == AR_INT32 || d == AR_FLOAT32 || d == AR_BFL
 bool valid_op(int o) { return o == AR_SUM || o == AR_MAX || o == AR_AVG; }
 bool valid_algo(int a) {
     return a == AR_ALGO_RING_STEP || a == AR_ALGO_RING_FUSED || a == AR_ALGO_TREE ||
-           a == AR_ALGO_HALVING_DOUBLING || a == AR_ALGO_AUTO;
+           a == AR_ALGO_HALVING_DOUBLING || a == AR_ALGO_AUTO || a == AR_ALGO_DOUBLE_TREE;
 }
 int log2_exact(int n) {
     int l = 0;
@@ -140,6 +140,12 @@ double predict_allreduce_us(int algo, int n, size_t count, size_t eb) {
         case AR_ALGO_TREE:
             return kCallUs + (log2_ceil(n) - 1) * kLaunchUs +
                    2.0 * n * k * log2_ceil(n) / (kTreeGBps * 1e3);
+        case AR_ALGO_DOUBLE_TREE:
+            // per tree (half the vector, H = K/2): N/2-1 interior nodes read 3H and
+            // write H going up and read H / write 2H going down; the root steps
+            // move 3H and 2H.  Both trees: (7 (N/2 - 1) + 5) K.
+            return kCallUs + (2.0 * log2_ceil(n) - 1) * kLaunchUs +
+                   (7.0 * (n / 2 - 1) + 5.0) * k / (kStepGBps * 1e3);
     }
     return 1e300;
 }
@@ -147,9 +153,10 @@ double predict_allreduce_us(int algo, int n, size_t count, size_t eb) {
 int auto_algo(int n, size_t count, size_t eb) {
     int best = AR_ALGO_RING_FUSED;
     double best_us = predict_allreduce_us(best, n, count, eb);
-    const int cands[] = {AR_ALGO_RING_STEP, AR_ALGO_HALVING_DOUBLING, AR_ALGO_TREE};
+    const int cands[] = {AR_ALGO_RING_STEP, AR_ALGO_HALVING_DOUBLING, AR_ALGO_TREE,
+                         AR_ALGO_DOUBLE_TREE};
     for (int a : cands) {
-        if ((a == AR_ALGO_TREE || a == AR_ALGO_HALVING_DOUBLING) && !pow2(n)) continue;
+        if (a != AR_ALGO_RING_STEP && !pow2(n)) continue;
         const double t = predict_allreduce_us(a, n, count, eb);
         if (t < best_us) {
             best_us = t;
@@ -324,22 +331,23 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
         if (algo == AR_ALGO_AUTO) {
             // ReduceScatter / AllGather alone follow the AllReduce choice, minus TREE
             algo = auto_algo(nranks, count, elem_bytes((ar_dtype)dtype));
-            if (algo == AR_ALGO_TREE && coll != COLL_AR) algo = AR_ALGO_RING_FUSED;
+            if ((algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE) && coll != COLL_AR)
+                algo = AR_ALGO_RING_FUSED;
             if (debug_enabled()) std::fprintf(stderr, "[ar] AUTO -> algo %d\n", algo);
         }
-        if (algo == AR_ALGO_TREE && coll != COLL_AR)
+        if ((algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE) && coll != COLL_AR)
             return fail(ctx, AR_ERR_UNSUPPORTED,
-                        "TREE is an AllReduce algorithm; use RING_STEP, RING_FUSED or "
-                        "HALVING_DOUBLING");
-        if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING) && !pow2(nranks))
-            return fail(ctx, AR_ERR_UNSUPPORTED,
-                        "%s needs a power-of-two nranks, got %d",
-                        algo == AR_ALGO_TREE ? "TREE (recursive doubling)" : "HALVING_DOUBLING",
-                        nranks);
+                        "TREE and DOUBLE_TREE are AllReduce algorithms; use RING_STEP, "
+                        "RING_FUSED or HALVING_DOUBLING");
+        if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING ||
+             algo == AR_ALGO_DOUBLE_TREE) && !pow2(nranks))
+            return fail(ctx, AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two nranks, got %d",
+                        algo, nranks);
         if (count == 0 || nranks == 1) return AR_OK;
         const arlib::Kind probe = algo == AR_ALGO_TREE ? arlib::KIND_TREE_STEP
                                   : algo == AR_ALGO_HALVING_DOUBLING ? arlib::KIND_HD_AG_STEP
-                                                                     : arlib::KIND_RS_STEP;
+                                  : algo == AR_ALGO_DOUBLE_TREE ? arlib::KIND_DT_STEP
+                                                                : arlib::KIND_RS_STEP;
         s = check_shape(ctx, probe, dtype, nranks, count, vec,
                         algo == AR_ALGO_HALVING_DOUBLING ? log2_exact(nranks) - 1 : 0);
         if (s != AR_OK) return s;
@@ -369,6 +377,14 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
                                            vec, mis), t);
                     if (s != AR_OK) return s;
                 }
+            }
+            return AR_OK;
+        }
+        if (algo == AR_ALGO_DOUBLE_TREE) {
+            for (int st = 0; st < 2 * log2_exact(nranks); ++st) {
+                s = run(ctx, make_plan(arlib::KIND_DT_STEP, dtype, o, nranks, count, st, vec, mis),
+                        t);
+                if (s != AR_OK) return s;
             }
             return AR_OK;
         }
@@ -414,11 +430,11 @@ ar_status single_step(ar_ctx* ctx, arlib::Kind kind, void* const* bufs, int nran
         if (s != AR_OK) return s;
         int nsteps = nranks - 1;
         if (kind == arlib::KIND_TREE_STEP || kind == arlib::KIND_HD_RS_STEP ||
-            kind == arlib::KIND_HD_AG_STEP) {
+            kind == arlib::KIND_HD_AG_STEP || kind == arlib::KIND_DT_STEP) {
             if (!pow2(nranks))
                 return fail(ctx, AR_ERR_UNSUPPORTED,
                             "this step needs a power-of-two nranks, got %d", nranks);
-            nsteps = log2_exact(nranks);
+            nsteps = log2_exact(nranks) * (kind == arlib::KIND_DT_STEP ? 2 : 1);
         }
         if (step < 0 || step >= nsteps)
             return fail(ctx, AR_ERR_INVALID_ARG, "step %d outside [0, %d)", step, nsteps);
@@ -506,11 +522,17 @@ ar_status ar_hd_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
                        step);
 }
 
+ar_status ar_dtree_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                        ar_dtype dtype, ar_op op, int step) {
+    return single_step(ctx, arlib::KIND_DT_STEP, bufs, nranks, count, (int)dtype, (int)op, step);
+}
+
 ar_status ar_predict_us(ar_algo algo, int nranks, size_t count, ar_dtype dtype, double* us) {
     if (!us || nranks < 1 || nranks > AR_MAX_RANKS || !valid_dtype((int)dtype) ||
         !valid_algo((int)algo) || algo == AR_ALGO_AUTO)
         return AR_ERR_INVALID_ARG;
-    if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING) && !pow2(nranks))
+    if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING ||
+         algo == AR_ALGO_DOUBLE_TREE) && !pow2(nranks))
         return AR_ERR_UNSUPPORTED;
     *us = predict_allreduce_us((int)algo, nranks, count, elem_bytes(dtype));
     return AR_OK;

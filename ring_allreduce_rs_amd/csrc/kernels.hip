@@ -30,6 +30,9 @@
 //                  recursive-halving ReduceScatter and recursive-doubling
 //                  AllGather steps (the same page's "Recursive Doubling /
 //                  Halving", read as the bandwidth-optimal variant).
+//   k_dtree_step   one level of the double binary tree (two complementary
+//                  trees, each reducing half the vector up and broadcasting
+//                  it down).
 //   k_copy         plain 16-byte copy, the bandwidth / counter calibration.
 //
 // Block -> work mapping: block b handles tile (b mod tiles) of chunk
@@ -415,6 +418,133 @@ __global__ __launch_bounds__(kThreads) void k_hd_ag_step(const Args a) {
                                       false, a.nf, a.inv);
 }
 
+// ---------------------------------------------------------------- double binary tree
+//
+// Two complementary in-order binary trees ("AllReduce", compassingai.com,
+// section 3: reduce leaves-to-root, broadcast root-to-leaves; the double tree
+// runs two disjoint trees at once, each with part of the data).  Shape on
+// positions 0..N-1 (N a power of two): position 0 is the root with the single
+// child N/2; position v with lowest set bit b > 1 has children v - b/2 and
+// v + b/2.  Tree 0 places rank v at position v and carries elements
+// [0, ceil(count/2)); tree 1 places rank (v-1) mod N at position v and
+// carries the rest.  Steps (L = log2 N):
+//   s <  L-1  reduce level l = s+1: node v <- (left (+) own) (+) right
+//   s == L-1  root: node 0 <- own (+) node N/2, AVG divides here
+//   s == L    node N/2 <- node 0
+//   s >  L    broadcast level l = 2L-s: both children <- node v
+
+enum DtMode { DT_REDUCE3 = 0, DT_REDUCE2 = 1, DT_COPY1 = 2, DT_COPY2 = 3 };
+
+// a, b, c are left child / own (parent) / right child (REDUCE3, COPY2) or
+// unused / own / child (REDUCE2, COPY1).
+template <class Op, bool VEC, int MODE>
+__device__ __forceinline__ void dt_units(char* a, char* b, char* c, size_t byte0, size_t ubase,
+                                         size_t units, bool fin, float nf, float inv) {
+    using X = Unit<Op, VEC, kStepNT>;
+    using T = typename X::T;
+    bool ok[kUnroll];
+    size_t off[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t idx = ubase + (size_t)u * kThreads;
+        ok[u] = idx < units;
+        off[u] = byte0 + idx * X::kBytes;
+    }
+    T x[kUnroll], y[kUnroll], z[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        y[u] = ok[u] ? X::ld(b + off[u]) : X::zero();
+        if constexpr (MODE == DT_REDUCE3) x[u] = ok[u] ? X::ld(a + off[u]) : X::zero();
+        if constexpr (MODE == DT_REDUCE3 || MODE == DT_REDUCE2)
+            z[u] = ok[u] ? X::ld(c + off[u]) : X::zero();
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (!ok[u]) continue;
+        if constexpr (MODE == DT_REDUCE3) {
+            X::st(b + off[u], X::comb(X::comb(x[u], y[u]), z[u]));
+        } else if constexpr (MODE == DT_REDUCE2) {
+            T r = X::comb(y[u], z[u]);
+            if (fin) r = X::fin(r, nf, inv);
+            X::st(b + off[u], r);
+        } else if constexpr (MODE == DT_COPY1) {
+            X::st(c + off[u], y[u]);
+        } else {
+            X::st(a + off[u], y[u]);
+            X::st(c + off[u], y[u]);
+        }
+    }
+}
+
+template <class Op, bool VEC, int MODE>
+__device__ __forceinline__ void dt_range(char* a, char* b, char* c, size_t lo, size_t len,
+                                         unsigned mis, unsigned tile, bool fin, float nf,
+                                         float inv) {
+    constexpr int EB = Op::kElemBytes;
+    const Span sp = make_span<EB, VEC>(lo, len, mis);
+    const size_t ubase = (size_t)tile * (kThreads * kUnroll) + threadIdx.x;
+    if (ubase < sp.units)
+        dt_units<Op, VEC, MODE>(a, b, c, sp.body * EB, ubase, sp.units, fin, nf, inv);
+    if constexpr (VEC) {
+        if (tile == 0) {
+            const unsigned t = threadIdx.x;
+            if (t < sp.nhead)
+                dt_units<Op, false, MODE>(a, b, c, (lo + t) * EB, 0, 1, fin, nf, inv);
+            else if (t >= kTailLane && t - kTailLane < sp.ntail)
+                dt_units<Op, false, MODE>(a, b, c, (sp.tail + (t - kTailLane)) * EB, 0, 1, fin,
+                                          nf, inv);
+        }
+    }
+}
+
+__device__ __forceinline__ int dt_rank(int tree, int v, int n) {
+    return tree == 0 ? v : ((v - 1) & (n - 1));
+}
+
+// One double-tree step; block b = (tree, node j, tile) with `tiles` tiles per node.
+template <class Op, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_dtree_step(const Args a) {
+    const int n = a.n;
+    const int L = 31 - __builtin_clz((unsigned)n);
+    const int s = a.step;
+    const unsigned g = blockIdx.x / a.tiles;
+    const unsigned tile = blockIdx.x - g * a.tiles;
+    int lvl, mode;
+    if (s < L - 1) { lvl = s + 1; mode = DT_REDUCE3; }
+    else if (s == L - 1) { lvl = L; mode = DT_REDUCE2; }
+    else if (s == L) { lvl = L; mode = DT_COPY1; }
+    else { lvl = 2 * L - s; mode = DT_COPY2; }
+    const unsigned nodes = (mode == DT_REDUCE3 || mode == DT_COPY2) ? (unsigned)(n >> (lvl + 1)) : 1u;
+    const int tree = (int)(g / nodes);
+    const int j = (int)(g - (unsigned)tree * nodes);
+    const size_t half = (a.count + 1) / 2;
+    const size_t lo = tree == 0 ? 0 : half;
+    const size_t len = tree == 0 ? half : a.count - half;
+    if (len == 0) return;
+    if (mode == DT_REDUCE3 || mode == DT_COPY2) {
+        const int v = (2 * j + 1) << lvl;
+        const int hb = 1 << (lvl - 1);
+        char* left = rank_ptr(a, dt_rank(tree, v - hb, n));
+        char* own = rank_ptr(a, dt_rank(tree, v, n));
+        char* right = rank_ptr(a, dt_rank(tree, v + hb, n));
+        if (mode == DT_REDUCE3)
+            dt_range<Op, VEC, DT_REDUCE3>(left, own, right, lo, len, a.mis, tile, false, a.nf,
+                                          a.inv);
+        else
+            dt_range<Op, VEC, DT_COPY2>(left, own, right, lo, len, a.mis, tile, false, a.nf,
+                                        a.inv);
+    } else {
+        char* root = rank_ptr(a, dt_rank(tree, 0, n));
+        char* child = rank_ptr(a, dt_rank(tree, n / 2, n));
+        if (mode == DT_REDUCE2)
+            dt_range<Op, VEC, DT_REDUCE2>(nullptr, root, child, lo, len, a.mis, tile,
+                                          a.avg != 0, a.nf, a.inv);
+        else
+            dt_range<Op, VEC, DT_COPY1>(nullptr, root, child, lo, len, a.mis, tile, false, a.nf,
+                                        a.inv);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_copy(u32x4* __restrict__ dst,
                                                    const u32x4* __restrict__ src, size_t nvec) {
     const size_t base = (size_t)blockIdx.x * (kThreads * kCopyUnroll) + threadIdx.x;
@@ -447,6 +577,15 @@ bool plan_shape(const Plan& p, Shape* out) {
     if (p.kind == KIND_TREE_STEP) {
         tiles = ceil_div(ceil_div(p.count, epu), per_tile);
         groups = (size_t)p.nranks / 2;
+    } else if (p.kind == KIND_DT_STEP) {
+        int L = 0;
+        while ((1 << L) < p.nranks) ++L;
+        const int s = p.step;
+        size_t nodes = 1;
+        if (s < L - 1) nodes = (size_t)p.nranks >> (s + 2);
+        else if (s > L) nodes = (size_t)p.nranks >> (2 * L - s + 1);
+        tiles = ceil_div(ceil_div((p.count + 1) / 2, epu), per_tile);
+        groups = 2 * nodes;
     } else if (p.kind == KIND_HD_RS_STEP || p.kind == KIND_HD_AG_STEP) {
         // a step moves d consecutive chunks per rank
         const size_t per = ceil_div(p.count, (size_t)p.nranks);
@@ -495,6 +634,9 @@ static hipError_t launch_kind(const Plan& p, const Args& a, dim3 grid, hipStream
             break;
         case KIND_HD_RS_STEP:
             hipLaunchKernelGGL((k_hd_rs_step<Op, VEC>), grid, block, 0, s, a);
+            break;
+        case KIND_DT_STEP:
+            hipLaunchKernelGGL((k_dtree_step<Op, VEC>), grid, block, 0, s, a);
             break;
         default:
             return hipErrorInvalidValue;

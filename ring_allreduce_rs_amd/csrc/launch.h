@@ -24,6 +24,7 @@ enum Kind {
     KIND_TREE_STEP = 5,  // one recursive-doubling step
     KIND_HD_RS_STEP = 6, // one recursive-halving ReduceScatter step
     KIND_HD_AG_STEP = 7, // one recursive-doubling AllGather step
+    KIND_DT_STEP = 8,    // one double-binary-tree step (reduce up / broadcast down)
 };
 
 struct Plan {

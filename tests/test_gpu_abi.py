@@ -63,6 +63,7 @@ def test_invalid_arguments_are_rejected_before_launch(ctx):
         "tree step range": lambda: ctx.tree_step_ptrs(p, 64, "float32", "sum", 2),
         "hd rs step range": lambda: ctx.hd_rs_step_ptrs(p, 64, "float32", "sum", 2),
         "hd ag step range": lambda: ctx.hd_ag_step_ptrs(p, 64, "float32", -1),
+        "dtree step range": lambda: ctx.dtree_step_ptrs(p, 64, "float32", "sum", 4),
     }
     for name, fn in cases.items():
         assert status_of(fn) == INVALID, name
@@ -95,7 +96,11 @@ def test_unsupported_combinations(ctx):
                  lambda: ctx.reduce_scatter_ptrs(p3, 64, "float32", "sum", "halving_doubling"),
                  lambda: ctx.allgather_ptrs(p3, 64, "float32", "halving_doubling"),
                  lambda: ctx.hd_rs_step_ptrs(p3, 64, "float32", "sum", 0),
-                 lambda: ctx.hd_ag_step_ptrs(p3, 64, "float32", 0)):
+                 lambda: ctx.hd_ag_step_ptrs(p3, 64, "float32", 0),
+                 lambda: ctx.allreduce_ptrs(p3, 64, "float32", "sum", "double_tree"),
+                 lambda: ctx.dtree_step_ptrs(p3, 64, "float32", "sum", 0),
+                 lambda: ctx.reduce_scatter_ptrs(p4, 64, "float32", "sum", "double_tree"),
+                 lambda: ctx.allgather_ptrs(p4, 64, "float32", "double_tree")):
         assert status_of(call) == UNSUPPORTED
 
 
@@ -106,7 +111,7 @@ def test_noops(ctx):
     # one rank: AVG over one rank is the identity
     (t,) = bufs(1, count=1001)
     before = t.clone()
-    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling"):
+    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling", "double_tree", "auto"):
         ar.allreduce([t], op="avg", algo=algo)
     torch.cuda.synchronize()
     assert torch.equal(t, before)

@@ -93,6 +93,11 @@ def test_ddp_bucket_config_full_oracle():
     run(ts, "avg", "halving_doubling")
     assert ranks_identical(ts)
     assert_bits_equal(to_np(ts[0]), hw, "halving_doubling")
+    dw = oracle.simulate_double_tree_allreduce(xs, "float32", "avg").state[0]
+    ts = to_gpu(xs, "float32")
+    run(ts, "avg", "double_tree")
+    assert ranks_identical(ts)
+    assert_bits_equal(to_np(ts[0]), dw, "double_tree")
 
 
 @pytest.mark.slow
@@ -135,11 +140,13 @@ def test_sweep_config(w):
         a = W.device_inputs(w, seed=0)
         idx = sample_positions(w.count, w.nranks, k=4096, seed=2)
         vals = gather(a, idx)
-    b, c, h = clone_all(a), clone_all(a), clone_all(a)
+    b, c, h, d = clone_all(a), clone_all(a), clone_all(a), clone_all(a)
     run(a, "sum", "ring_step")
     run(b, "sum", "ring_fused")
     run(c, "sum", "tree")
     run(h, "sum", "halving_doubling")
+    run(d, "sum", "double_tree")
+    assert ranks_identical(d)
     for r in range(w.nranks):
         assert torch.equal(a[r], b[r]), f"fused != step on rank {r}"
     assert ranks_identical(a) and ranks_identical(c) and ranks_identical(h)
@@ -150,6 +157,9 @@ def test_sweep_config(w):
                           "tree")
         assert_bits_equal(to_np(h[0]), oracle.simulate_hd_allreduce(xs, "float32", "sum").state[0],
                           "halving_doubling")
+        assert_bits_equal(to_np(d[0]),
+                          oracle.simulate_double_tree_allreduce(xs, "float32", "sum").state[0],
+                          "double_tree")
     else:
         ring_want = oracle.ring_fold_at(vals, chunk_ids(idx, w.count, w.nranks), w.nranks,
                                         "float32", "sum")
@@ -158,7 +168,11 @@ def test_sweep_config(w):
         assert_bits_equal(gather(a[:1], idx)[0], ring_want, "ring sampled")
         assert_bits_equal(gather(c[:1], idx)[0], tree_want, "tree sampled")
         assert_bits_equal(gather(h[:1], idx)[0], hd_want, "hd sampled")
-    del a, b, c, h
+        half = (w.count + 1) // 2
+        dt_want = np.where(idx < half, oracle.dtree_fold_at(vals, 0, "float32", "sum"),
+                           oracle.dtree_fold_at(vals, 1, "float32", "sum"))
+        assert_bits_equal(gather(d[:1], idx)[0], dt_want, "double tree sampled")
+    del a, b, c, h, d
     torch.cuda.empty_cache()
 
 

@@ -181,9 +181,10 @@ def test_unaligned_buffers(dtype, op, shift, same_alignment):
     xs = rand_inputs(dtype, n, count, seed=shift + 17)
     wants = {"ring": oracle.simulate_ring_allreduce(xs, dtype, op).state,
              "tree": oracle.simulate_tree_allreduce(xs, dtype, op).state,
-             "halving_doubling": oracle.simulate_hd_allreduce(xs, dtype, op).state}
+             "halving_doubling": oracle.simulate_hd_allreduce(xs, dtype, op).state,
+             "double_tree": oracle.simulate_double_tree_allreduce(xs, dtype, op).state}
     stride = ((count + 64 + 7) // 8) * 8          # a multiple of 16 bytes per row
-    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling"):
+    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling", "double_tree"):
         want = wants["ring" if algo.startswith("ring") else algo]
         store = torch.zeros(n * stride, dtype=to_gpu(xs[:1], dtype)[0].dtype, device="cuda")
         views = []
@@ -226,7 +227,8 @@ def test_auto_runs_the_model_choice(dtype, op, n, count):
     pick = ar.auto_algo(n, count, dtype)
     sim = {"ring_fused": oracle.simulate_ring_allreduce, "ring_step": oracle.simulate_ring_allreduce,
            "tree": oracle.simulate_tree_allreduce,
-           "halving_doubling": oracle.simulate_hd_allreduce}[pick]
+           "halving_doubling": oracle.simulate_hd_allreduce,
+           "double_tree": oracle.simulate_double_tree_allreduce}[pick]
     want = sim(xs, dtype, op).state
     ts = to_gpu(xs, dtype)
     ar.allreduce(ts, op=op, algo="auto")
@@ -237,6 +239,33 @@ def test_auto_runs_the_model_choice(dtype, op, n, count):
     ar.reduce_scatter(rs, op=op, algo="auto")
     ar.allgather(rs, algo="auto")
     torch.cuda.synchronize()
-    if pick != "tree":
+    if pick not in ("tree", "double_tree"):
         for r in range(n):
             assert_bits_equal(to_np(rs[r]), want[r], f"auto RS+AG rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("n,count", [(1, 7), (2, 4099), (4, 6), (4, 24581), (8, 65539),
+                                     (16, 33), (16, 40003), (32, 2050), (2, 1)])
+def test_double_tree_allreduce_matches_oracle(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n * 19 + count)
+    want = oracle.simulate_double_tree_allreduce(xs, dtype, op).state
+    ts = to_gpu(xs, dtype)
+    ar.allreduce(ts, op=op, algo="double_tree")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), want[r], f"dtree {dtype} {op} n={n} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "max")])
+@pytest.mark.parametrize("n,count", [(2, 1001), (4, 24581), (8, 1000), (16, 40003), (8, 3)])
+def test_every_double_tree_step_matches_oracle_snapshot(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=count + 4)
+    snaps = oracle.simulate_double_tree_allreduce(xs, dtype, op, record=True).snapshots
+    assert len(snaps) == 2 * (n.bit_length() - 1)
+    ts = to_gpu(xs, dtype)
+    for s in range(len(snaps)):
+        ar.dtree_step(ts, op, s)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), snaps[s][r], f"dtree step {s} rank {r}")
