@@ -40,8 +40,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 INFINITY_CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# the sources the fused kernel and the calibration copy are built from
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_rs_amd", "csrc", f)
-                  for f in ("kernels.hip", "elem.h")]
+                  for f in ("common.h", "elem.h", "fused.hip", "copy.hip")]
 
 
 def kernel_source_hash() -> str:

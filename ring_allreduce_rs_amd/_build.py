@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libar.so")
 
-SOURCES = ["kernels.hip", "ar_api.cpp"]
+SOURCES = ["fused.hip", "steps.hip", "copy.hip", "dispatch.hip", "ar_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -1,7 +1,7 @@
 // ar_api.cpp -- the C ABI declared in include/ar.h: argument validation,
-// chunk layout, algorithm dispatch and error reporting.  Kernels live in
-// kernels.hip; this file only decides what to launch, in which order, on the
-// context's stream.
+// chunk layout, algorithm dispatch, the cost model behind AR_ALGO_AUTO and
+// error reporting.  Kernels live in fused.hip and steps.hip; this file only
+// decides what to launch, in which order, on the context's stream.
 //
 // The ring AllReduce is ReduceScatter (N-1 steps) followed by AllGather (N-1
 // steps) ("AllReduce 集合通信", zzmblog.top, sections 语义 and 两阶段流程); the

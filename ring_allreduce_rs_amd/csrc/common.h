@@ -1,0 +1,136 @@
+// common.h -- shared device-side building blocks of the AllReduce kernels
+// (gfx950): launch-shape constants, the kernel argument block, 16-byte /
+// element-wise memory units and the head / body / tail split of a range.
+#pragma once
+
+#include "elem.h"
+#include "launch.h"
+
+namespace arlib {
+
+#ifndef AR_FUSED_NT
+#define AR_FUSED_NT 1
+#endif
+#ifndef AR_STEP_NT
+#define AR_STEP_NT 0
+#endif
+
+#ifndef AR_FUSED_THREADS
+#define AR_FUSED_THREADS 64
+#endif
+#ifndef AR_FUSED_UNROLL
+#define AR_FUSED_UNROLL 4
+#endif
+#ifndef AR_SPECIALIZE_N
+#define AR_SPECIALIZE_N 1
+#endif
+
+constexpr int kThreads = 256;       // per-step kernels: 4 wavefronts of 64
+constexpr int kUnroll = 2;          // per-step kernels: 16-byte units per lane per tile
+constexpr int kFusedThreads = AR_FUSED_THREADS;
+constexpr int kFusedUnroll = AR_FUSED_UNROLL;
+constexpr int kBatch = 8;           // ranks of loads issued before they are folded
+constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
+// Streaming (non-temporal) loads and stores.  The fused kernel touches every
+// byte once, so caching it only evicts useful lines: on MI355X 8 x 25 MiB went
+// from 86 us to 77 us with both loads and stores streaming.  The per-step
+// kernels are the opposite case: each step re-reads what the previous step
+// wrote, and a 200 MiB working set stays in the 256 MB Infinity Cache when
+// the stores are ordinary (ring 8 x 25 MiB: 169 us with, 189 us without).
+constexpr bool kFusedNT = AR_FUSED_NT != 0;
+constexpr bool kStepNT = AR_STEP_NT != 0;
+constexpr int kCopyUnroll = 1;  // the plain copy streams best with one unit per lane
+
+struct Args {
+    RankTable t;
+    size_t count;     // elements per rank
+    size_t per;       // chunk length L = ceil(count / N)
+    int n;            // ranks
+    int step;         // step index (per-step kernels)
+    unsigned tiles;   // tiles per chunk (per pair for the tree)
+    unsigned mis;     // every buffer's address mod 16, in bytes
+    int avg;          // 1: divide the finished sum by n
+    float nf;         // (float)n
+    float inv;        // 1/n when n is a power of two (exact), else 0
+};
+
+template <class Op, bool VEC, bool NT = false>
+struct Unit;
+
+template <class Op, bool NT>
+struct Unit<Op, true, NT> {
+    using T = u32x4;
+    static constexpr int kBytes = 16;
+    __device__ static T ld(const char* p) { return ld16<NT>(p); }
+    __device__ static void st(char* p, T v) { st16<NT>(p, v); }
+    __device__ static T comb(T a, T b) { return comb4<Op>(a, b); }
+    __device__ static T fin(T a, float nf, float inv) { return finish4<Op>(a, nf, inv); }
+    __device__ static T zero() { return u32x4{0u, 0u, 0u, 0u}; }
+};
+
+template <class Op, bool NT>
+struct Unit<Op, false, NT> {
+    using T = uint32_t;
+    static constexpr int kBytes = Op::kElemBytes;
+    __device__ static T ld(const char* p) { return ld_elem<Op::kElemBytes>(p); }
+    __device__ static void st(char* p, T v) { st_elem<Op::kElemBytes>(p, v); }
+    __device__ static T comb(T a, T b) { return Op::comb_elem(a, b); }
+    __device__ static T fin(T a, float nf, float inv) { return Op::finish_elem(a, nf, inv); }
+    __device__ static T zero() { return 0u; }
+};
+
+// Split the element range [lo, lo+len) into an element-wise head up to the
+// first 16-byte boundary, a body of 16-byte units, and an element-wise tail.
+struct Span {
+    size_t body;     // first element of the body
+    size_t units;    // body length in units
+    size_t tail;     // first tail element
+    unsigned nhead;  // head elements, starting at lo
+    unsigned ntail;  // tail elements
+};
+
+template <int EB, bool VEC>
+__device__ __forceinline__ Span make_span(size_t lo, size_t len, unsigned mis) {
+    Span s;
+    if constexpr (VEC) {
+        constexpr int kEpu = 16 / EB;
+        const unsigned m = (unsigned)((mis + lo * EB) & 15u);
+        size_t h = m ? (16u - m) / EB : 0;
+        if (h > len) h = len;
+        s.nhead = (unsigned)h;
+        s.body = lo + h;
+        s.units = (len - h) / kEpu;
+        s.tail = s.body + s.units * kEpu;
+        s.ntail = (unsigned)(lo + len - s.tail);
+    } else {
+        s.nhead = 0;
+        s.body = lo;
+        s.units = len;
+        s.tail = lo + len;
+        s.ntail = 0;
+    }
+    return s;
+}
+
+__device__ __forceinline__ void chunk_bounds(const Args& a, int c, size_t& lo, size_t& len) {
+    size_t b0 = (size_t)c * a.per;
+    if (b0 > a.count) b0 = a.count;
+    size_t b1 = b0 + a.per;
+    if (b1 > a.count) b1 = a.count;
+    lo = b0;
+    len = b1 - b0;
+}
+
+__device__ __forceinline__ char* rank_ptr(const Args& a, int r) {
+    return reinterpret_cast<char*>(a.t.p[r]);
+}
+
+inline int elem_bytes(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
+
+inline size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
+
+// Launchers, one per translation unit.
+hipError_t launch_fused_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+hipError_t launch_step_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+
+}  // namespace arlib

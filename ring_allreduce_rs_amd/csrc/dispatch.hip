@@ -1,0 +1,67 @@
+// dispatch.hip -- launch shapes and the Plan -> kernel-argument translation
+// shared by every kernel family (host code).
+#include "common.h"
+
+namespace arlib {
+
+bool plan_shape(const Plan& p, Shape* out) {
+    const size_t eb = (size_t)elem_bytes(p.dtype);
+    const size_t epu = p.vec ? 16 / eb : 1;
+    const bool fused = p.kind == KIND_FUSED_AR || p.kind == KIND_FUSED_RS || p.kind == KIND_FUSED_AG;
+    const size_t threads = fused ? kFusedThreads : kThreads;
+    const size_t per_tile = threads * (fused ? kFusedUnroll : kUnroll);
+    size_t tiles, groups;
+    if (p.kind == KIND_TREE_STEP) {
+        tiles = ceil_div(ceil_div(p.count, epu), per_tile);
+        groups = (size_t)p.nranks / 2;
+    } else if (p.kind == KIND_DT_STEP) {
+        int L = 0;
+        while ((1 << L) < p.nranks) ++L;
+        const int s = p.step;
+        size_t nodes = 1;
+        if (s < L - 1) nodes = (size_t)p.nranks >> (s + 2);
+        else if (s > L) nodes = (size_t)p.nranks >> (2 * L - s + 1);
+        tiles = ceil_div(ceil_div((p.count + 1) / 2, epu), per_tile);
+        groups = 2 * nodes;
+    } else if (p.kind == KIND_HD_RS_STEP || p.kind == KIND_HD_AG_STEP) {
+        // a step moves d consecutive chunks per rank
+        const size_t per = ceil_div(p.count, (size_t)p.nranks);
+        const size_t d = p.kind == KIND_HD_RS_STEP ? ((size_t)p.nranks >> (p.step + 1))
+                                                   : ((size_t)1 << p.step);
+        tiles = ceil_div(ceil_div(per * d, epu), per_tile);
+        groups = (size_t)p.nranks;
+    } else {
+        const size_t per = ceil_div(p.count, (size_t)p.nranks);
+        tiles = ceil_div(ceil_div(per, epu), per_tile);
+        groups = (size_t)p.nranks;
+    }
+    if (tiles == 0) tiles = 1;
+    const size_t blocks = tiles * groups;
+    if (blocks == 0 || blocks > 0x7fffffffu || tiles > 0xffffffffu) return false;
+    out->blocks = (unsigned)blocks;
+    out->threads = (unsigned)threads;
+    out->tiles = (unsigned)tiles;
+    return true;
+}
+
+hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream) {
+    Shape sh;
+    if (!plan_shape(p, &sh)) return hipErrorInvalidConfiguration;
+    Args a;
+    a.t = t;
+    a.count = p.count;
+    a.per = ceil_div(p.count, (size_t)p.nranks);
+    a.n = p.nranks;
+    a.step = p.step;
+    a.tiles = sh.tiles;
+    a.mis = p.mis;
+    a.avg = p.op == AR_AVG ? 1 : 0;
+    a.nf = (float)p.nranks;
+    a.inv = (p.nranks & (p.nranks - 1)) == 0 ? 1.0f / (float)p.nranks : 0.0f;
+    const dim3 grid(sh.blocks);
+
+    const bool fused = p.kind == KIND_FUSED_AR || p.kind == KIND_FUSED_RS || p.kind == KIND_FUSED_AG;
+    return fused ? launch_fused_kind(p, a, grid, stream) : launch_step_kind(p, a, grid, stream);
+}
+
+}  // namespace arlib

@@ -1,5 +1,6 @@
 // launch.h -- internal interface between the C-ABI host layer (ar_api.cpp)
-// and the HIP kernels (kernels.hip).  Not part of the public ABI.
+// and the HIP kernels (fused.hip, steps.hip, copy.hip, dispatch.hip).  Not
+// part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
