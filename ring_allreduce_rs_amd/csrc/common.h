@@ -30,6 +30,30 @@ constexpr int kUnroll = 2;          // per-step kernels: 16-byte units per lane 
 constexpr int kFusedThreads = AR_FUSED_THREADS;
 constexpr int kFusedUnroll = AR_FUSED_UNROLL;
 constexpr int kBatch = 8;           // ranks of loads issued before they are folded
+// Fused-kernel shapes (units of 16 bytes per lane, ranks of loads in flight
+// before folding).  WIDE suits 8 ranks; with many ranks the fold would wait on
+// memory N/8 times, so DEEP keeps 32 ranks of loads in flight (a 64-rank fold
+// waits twice); MID sits between for 9-16 ranks.  fused_variant() picks one.
+#ifndef AR_FUSED_FORCE_CFG
+#define AR_FUSED_FORCE_CFG -1
+#endif
+#ifndef AR_FUSED_DEEP_MAX_CHUNK_BYTES
+#define AR_FUSED_DEEP_MAX_CHUNK_BYTES (256u << 10)
+#endif
+
+struct FusedWide {
+    static constexpr int U = kFusedUnroll;
+    static constexpr int B = kBatch;
+};
+struct FusedDeep {
+    static constexpr int U = 1;
+    static constexpr int B = 32;
+};
+struct FusedMid {
+    static constexpr int U = 2;
+    static constexpr int B = 16;
+};
+enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_MID = 2 };
 constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
 // Streaming (non-temporal) loads and stores.  The fused kernel touches every
 // byte once, so caching it only evicts useful lines: on MI355X 8 x 25 MiB went
@@ -128,6 +152,10 @@ __device__ __forceinline__ char* rank_ptr(const Args& a, int r) {
 inline int elem_bytes(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
 
 inline size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
+
+// Which fused shape (CFG_*) a plan runs (host side; dispatch.hip).
+int fused_variant(const Plan& p);
+int fused_units_per_lane(int cfg);
 
 // Launchers, one per translation unit.
 hipError_t launch_fused_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s);

@@ -4,12 +4,32 @@
 
 namespace arlib {
 
+int fused_variant(const Plan& p) {
+    if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return CFG_WIDE;
+    if (AR_FUSED_FORCE_CFG >= 0) return AR_FUSED_FORCE_CFG;
+    // Measured on MI355X (fused AllReduce, inputs cold in HBM): WIDE is best
+    // for fp32 / int32 at 8 and 16 ranks (8 x 25 MiB: 74 us vs 83 us DEEP;
+    // 16 x 1 GiB: 6.9 ms vs 7.7 ms); DEEP for 64 ranks (64 x 64 MiB: 1.60 ms
+    // vs 1.88 ms) and for bf16, whose per-hop rounding makes the fold
+    // ALU-heavier and favours the higher occupancy (8 x 2 GiB: 5.97 ms vs
+    // 6.39 ms); small chunks are latency-bound and also favour DEEP.
+    if (p.dtype == AR_BFLOAT16 || p.nranks > 16) return CFG_DEEP;
+    if (p.nranks <= kBatch) return CFG_WIDE;
+    const size_t per = ceil_div(p.count, (size_t)p.nranks) * (size_t)elem_bytes(p.dtype);
+    return per <= (size_t)AR_FUSED_DEEP_MAX_CHUNK_BYTES ? CFG_DEEP : CFG_WIDE;
+}
+
+int fused_units_per_lane(int cfg) {
+    return cfg == CFG_DEEP ? FusedDeep::U : cfg == CFG_MID ? FusedMid::U : FusedWide::U;
+}
+
 bool plan_shape(const Plan& p, Shape* out) {
     const size_t eb = (size_t)elem_bytes(p.dtype);
     const size_t epu = p.vec ? 16 / eb : 1;
     const bool fused = p.kind == KIND_FUSED_AR || p.kind == KIND_FUSED_RS || p.kind == KIND_FUSED_AG;
     const size_t threads = fused ? kFusedThreads : kThreads;
-    const size_t per_tile = threads * (fused ? kFusedUnroll : kUnroll);
+    const size_t per_tile =
+        threads * (fused ? (size_t)fused_units_per_lane(fused_variant(p)) : (size_t)kUnroll);
     size_t tiles, groups;
     if (p.kind == KIND_TREE_STEP) {
         tiles = ceil_div(ceil_div(p.count, epu), per_tile);

@@ -37,17 +37,33 @@ __device__ __forceinline__ uint32_t fmaximum_bits(uint32_t a, uint32_t b) {
     return fa > fb ? a : b;
 }
 
-// binary32 -> bf16, round to nearest, ties to even, on the bit pattern:
-// adding 0x7FFF plus the lowest kept bit carries into the kept half exactly
-// when the dropped half exceeds one half, or equals it with an odd kept half.
-// NaN -> canonical quiet NaN 0x7FC0.
+// binary32 -> bf16, round to nearest, ties to even; NaN -> canonical quiet
+// NaN 0x7FC0.  gfx950 converts with v_cvt_pk_bf16_f32 (two values per
+// instruction).  Its result was compared on MI355X with the integer rule --
+// add 0x7FFF plus the lowest kept bit, drop 16 bits -- for all 2^32 fp32 bit
+// patterns: identical for every non-NaN input (subnormals, overflow by
+// rounding and ties included); NaN inputs keep their sign and payload there,
+// so they are replaced by 0x7FC0 here.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = as_u32(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t h = __builtin_bit_cast(uint16_t, (__bf16)f);
+    return f != f ? 0x7fc0u : h;
+}
+
+// Two values rounded at once: lo into bits 0..15, hi into bits 16..31.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    const f32x2_t f = {lo, hi};
+    uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    if (lo != lo) r = (r & 0xffff0000u) | 0x7fc0u;
+    if (hi != hi) r = (r & 0x0000ffffu) | 0x7fc00000u;
+    return r;
 }
 
 __device__ __forceinline__ float bf16_widen(uint32_t h) { return as_f32(h << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xffff0000u); }
 
 // x / n, correctly rounded.  When n is a power of two the caller passes
 // inv = 1/n (exact); x * 2^-k and x / 2^k are then the same real number
@@ -109,10 +125,10 @@ struct OpBF16Sum {
         return bf16_rne(div_by_n(bf16_widen(a & 0xffffu), nf, inv));
     }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) {
-        return comb_elem(a, b) | (comb_elem(a >> 16, b >> 16) << 16);
+        return bf16x2_rne(__fadd_rn(bf16_lo(a), bf16_lo(b)), __fadd_rn(bf16_hi(a), bf16_hi(b)));
     }
     __device__ static uint32_t finish_word(uint32_t a, float nf, float inv) {
-        return finish_elem(a, nf, inv) | (finish_elem(a >> 16, nf, inv) << 16);
+        return bf16x2_rne(div_by_n(bf16_lo(a), nf, inv), div_by_n(bf16_hi(a), nf, inv));
     }
 };
 

@@ -21,16 +21,18 @@
 
 namespace arlib {
 
-// Units ubase, ubase+kFusedThreads, ... (kFusedUnroll of them, bounded by
-// `units`) of the range starting at byte offset byte0 in every rank buffer.
-// NR > 0 fixes the rank count at compile time (loops fully unrolled); NR == 0
-// reads it from the arguments.
-template <class Op, int MODE, bool VEC, int NR>
+// Units ubase, ubase+kFusedThreads, ... (CFG::U of them, bounded by `units`)
+// of the range starting at byte offset byte0 in every rank buffer; CFG::B
+// ranks of loads are issued before they are folded.  NR > 0 fixes the rank
+// count at compile time (loops fully unrolled); NR == 0 reads it from the
+// arguments.
+template <class Op, int MODE, bool VEC, int NR, class CFG>
 __device__ __forceinline__ void fused_units(const Args& a, int c, int start, size_t byte0,
                                             size_t ubase, size_t units) {
     using X = Unit<Op, VEC, kFusedNT>;
     using T = typename X::T;
-    constexpr int U = kFusedUnroll;
+    constexpr int U = CFG::U;
+    constexpr int kB = CFG::B;
     const int n = NR > 0 ? NR : a.n;
     bool ok[U];
     size_t off[U];
@@ -57,12 +59,12 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
         // ring order: start = c+1, then c+2, ..., ending with c itself
         int r = start;
 #pragma unroll
-        for (int j0 = 0; j0 < (NR > 0 ? NR : AR_MAX_RANKS); j0 += kBatch) {
+        for (int j0 = 0; j0 < (NR > 0 ? NR : AR_MAX_RANKS); j0 += kB) {
             if (NR == 0 && j0 >= n) break;
-            T v[kBatch][U];
+            T v[kB][U];
             int rr = r;
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
+            for (int j = 0; j < kB; ++j) {
                 if (j0 + j < n) {
                     const char* src = rank_ptr(a, rr);
 #pragma unroll
@@ -72,7 +74,7 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
                 }
             }
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
+            for (int j = 0; j < kB; ++j) {
                 if (j0 + j < n) {
 #pragma unroll
                     for (int u = 0; u < U; ++u)
@@ -103,7 +105,7 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
     }
 }
 
-template <class Op, int MODE, bool VEC, int NR>
+template <class Op, int MODE, bool VEC, int NR, class CFG>
 __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
     constexpr int EB = Op::kElemBytes;
     const int n = NR > 0 ? NR : a.n;
@@ -114,18 +116,18 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
     if (len == 0) return;
     const Span sp = make_span<EB, VEC>(lo, len, a.mis);
     const int start = (c + 1 == n) ? 0 : c + 1;
-    const size_t ubase = (size_t)tile * (kFusedThreads * kFusedUnroll) + threadIdx.x;
+    const size_t ubase = (size_t)tile * (kFusedThreads * CFG::U) + threadIdx.x;
     if (ubase < sp.units)
-        fused_units<Op, MODE, VEC, NR>(a, c, start, sp.body * EB, ubase, sp.units);
+        fused_units<Op, MODE, VEC, NR, CFG>(a, c, start, sp.body * EB, ubase, sp.units);
     if constexpr (VEC) {
         // heads have at most 15 bytes (< 8 elements), as do tails
         if (tile == 0) {
             const unsigned t = threadIdx.x;
             if (t < sp.nhead)
-                fused_units<Op, MODE, false, NR>(a, c, start, (lo + t) * EB, 0, 1);
+                fused_units<Op, MODE, false, NR, FusedDeep>(a, c, start, (lo + t) * EB, 0, 1);
             else if (t >= kTailLane && t - kTailLane < sp.ntail)
-                fused_units<Op, MODE, false, NR>(a, c, start, (sp.tail + (t - kTailLane)) * EB,
-                                                 0, 1);
+                fused_units<Op, MODE, false, NR, FusedDeep>(a, c, start,
+                                                            (sp.tail + (t - kTailLane)) * EB, 0, 1);
         }
     }
 }
@@ -133,10 +135,17 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
 template <class Op, int MODE, bool VEC>
 static void launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
     const dim3 block(kFusedThreads);
-    if (AR_SPECIALIZE_N && VEC && p.nranks == 8)
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0>), grid, block, 0, s, a);
+    const int cfg = fused_variant(p);
+    const bool n8 = AR_SPECIALIZE_N && VEC && p.nranks == 8;
+    if (cfg == CFG_DEEP) {
+        // the runtime-N loop measured faster than the 8-rank unrolled one here
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep>), grid, block, 0, s, a);
+    } else if (cfg == CFG_MID) {
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedMid>), grid, block, 0, s, a);
+    } else {
+        if (n8) hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedWide>), grid, block, 0, s, a);
+    }
 }
 
 template <class Op>
@@ -157,9 +166,11 @@ template <int EB>
 static hipError_t launch_fused_ag(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
     const dim3 block(kFusedThreads);
     if (p.vec)
-        hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 0>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 0, FusedWide>), grid, block, 0,
+                           s, a);
     else
-        hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, false, 0>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, false, 0, FusedWide>), grid, block,
+                           0, s, a);
     return hipGetLastError();
 }
 

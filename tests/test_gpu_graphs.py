@@ -1,0 +1,58 @@
+"""The library's calls can be captured in a HIP graph and replayed: they
+allocate nothing, never synchronise and record only kernel launches on the
+caller's stream.  Every replay is checked against the oracle, with eager work
+(re-loading the inputs) and synchronisations between replays."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_allreduce_rs_amd as ar
+from tests.gpu_helpers import assert_bits_equal, to_gpu, to_np
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SIMS = {"ring_step": oracle.simulate_ring_allreduce, "ring_fused": oracle.simulate_ring_allreduce,
+        "tree": oracle.simulate_tree_allreduce, "halving_doubling": oracle.simulate_hd_allreduce,
+        "double_tree": oracle.simulate_double_tree_allreduce}
+
+
+@pytest.mark.parametrize("algo", sorted(SIMS))
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "max")])
+def test_captured_allreduce_replays_match_oracle(algo, dtype, op):
+    n, count = 8, 12_347
+    rng = np.random.Generator(np.random.PCG64(count))
+    inputs = []
+    for rep in range(3):
+        if dtype == "int32":
+            xs = [rng.integers(-10**6, 10**6, size=count).astype(np.int32) for _ in range(n)]
+        else:
+            f = [rng.standard_normal(count).astype(np.float32) for _ in range(n)]
+            xs = f if dtype == "float32" else [
+                torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                for x in f]
+        inputs.append(xs)
+    src = [to_gpu(xs, dtype) for xs in inputs]
+    ts = [torch.empty_like(t) for t in src[0]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for t, s in zip(ts, src[0]):
+            t.copy_(s)
+        ar.allreduce(ts, op=op, algo=algo)         # warm-up on the capture stream
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            ar.allreduce(ts, op=op, algo=algo)
+    torch.cuda.synchronize()
+    for rep, xs in enumerate(inputs):
+        for t, s in zip(ts, src[rep]):                # eager work between replays
+            t.copy_(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = SIMS[algo](xs, dtype, op).state
+        for r in range(n):
+            assert_bits_equal(to_np(ts[r]), want[r], f"{algo} replay {rep} rank {r}")
