@@ -93,14 +93,14 @@ def parse():
     return a, names[a.workload]
 
 
-def time_algo(ar, sets, w, algo, steps, warmup):
-    """Time `steps` back-to-back launches.
+def time_algo(ar, sets, w, algo, steps, warmup, kind="allreduce"):
+    """Time `steps` back-to-back launches of one collective (`kind`).
 
     Returns (wall seconds between the two synchronisations, mean ms per
     launch from HIP events recorded on the launch stream at the start and the
     end of the timed region)."""
     import torch
-    calls = [ar.bind(ts, op=w.op, algo=algo) for ts in sets]
+    calls = [ar.bind(ts, op=w.op, algo=algo, kind=kind) for ts in sets]
     for i in range(warmup):
         calls[i % len(calls)]()
     start = torch.cuda.Event(enable_timing=True)
@@ -345,6 +345,20 @@ def main():
                 "GBps_algorithmic": round(alg_bytes * reps / wl / 1e9, 2),
                 "GBps_bytes_moved": round(step_bytes(w, algo) * reps / wl / 1e9, 2),
                 "event_us_per_allreduce": round(m * 1e3, 2),
+            }
+        # the two halves on their own (fused kernels): ReduceScatter reads every
+        # rank's chunks and writes the owner's (N*K + K bytes); AllGather reads
+        # the owners' chunks and writes the other N-1 copies (N*K bytes)
+        for kind, nbytes in (("reduce_scatter", (w.nranks + 1) * w.bytes_per_rank),
+                             ("allgather", w.nranks * w.bytes_per_rank)):
+            reps = max(5, min(args.steps // 4, 100))
+            wl, m = time_algo(ar, sets, w, "ring_fused", reps, 3, kind=kind)
+            others[kind + "_fused"] = {
+                "us_per_call": round(wl / reps * 1e6, 2),
+                "algorithmic_bytes": nbytes,
+                "GBps_algorithmic": round(nbytes * reps / wl / 1e9, 2),
+                "event_us_per_call": round(m * 1e3, 2),
+                "frac_hbm_peak": round(nbytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             }
         cg, cms = copy_ceiling(ar, w.nranks * w.bytes_per_rank)
         others["copy_ceiling"] = {"GBps": round(cg, 2), "bytes": 2 * w.nranks * w.bytes_per_rank,
