@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 INFINITY_CACHE_BYTES = 256 << 20
+ALWAYS_REPLAY = 1 << 62         # graph-replay threshold that covers every size measured
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # the sources the fused kernel and the calibration copy are built from
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_rs_amd", "csrc", f)
@@ -101,7 +102,9 @@ def time_algo(ar, sets, w, algo, steps, warmup, kind="allreduce"):
     end of the timed region)."""
     import torch
     calls = [ar.bind(ts, op=w.op, algo=algo, kind=kind) for ts in sets]
-    for i in range(warmup):
+    # every bucket set at least once before timing (with graph replay on, the
+    # first call on a set records its graph)
+    for i in range(max(warmup, len(calls))):
         calls[i % len(calls)]()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -193,9 +196,12 @@ def sweep(args):
 
     import ring_allreduce_rs_amd as ar
     import workloads as W
-    algos = ("ring_step", "tree", "halving_doubling", "double_tree", "ring_fused")
+    base = ("ring_step", "tree", "halving_doubling", "double_tree", "ring_fused")
+    # "+graph": the same algorithm replayed from a library-recorded HIP graph
+    algos = base + tuple(a + "+graph" for a in base[:4])
     launches = {"ring_step": 2 * 63, "tree": 6, "halving_doubling": 12, "double_tree": 12,
                 "ring_fused": 1}
+    launches.update({a + "+graph": launches[a] for a in base[:4]})
     rows = {a: [] for a in algos}
     for w in W.SWEEP:
         set_bytes = w.nranks * w.bytes_per_rank
@@ -203,7 +209,10 @@ def sweep(args):
         sets = [W.device_inputs(w, seed=s) for s in range(nsets)]
         steps = max(10, min(200, int(2e9 // max(set_bytes, 1))))
         for algo in algos:
-            wall, ms = time_algo(ar, sets, w, algo, steps, 5)
+            name, graph = algo.split("+")[0], algo.endswith("+graph")
+            ar.set_graphs(graph, max_bytes_per_rank=ALWAYS_REPLAY)
+            wall, ms = time_algo(ar, sets, w, name, steps, 5)
+            ar.set_graphs(False)
             t = wall / steps
             rows[algo].append((w.bytes_per_rank, t))
             print(json.dumps({"sweep": w.name, "algo": algo, "nranks": w.nranks,
@@ -211,7 +220,7 @@ def sweep(args):
                               "steps": steps, "us_per_allreduce": round(t * 1e6, 3),
                               "event_us": round(ms * 1e3, 3),
                               "GBps_algorithmic": round(2 * set_bytes / t / 1e9, 2),
-                              "GBps_bytes_moved": round(step_bytes(w, algo) / t / 1e9, 2)}),
+                              "GBps_bytes_moved": round(step_bytes(w, name) / t / 1e9, 2)}),
                   flush=True)
         del sets
         torch.cuda.empty_cache()
@@ -223,10 +232,11 @@ def sweep(args):
         fit[algo] = {"a_us": round(a * 1e6, 3), "b_us_per_MiB": round(b * 1e6 * (1 << 20), 4),
                      "alpha_us_per_launch": round(a * 1e6 / launches[algo], 3),
                      "launches": launches[algo],
-                     "bytes_moved_GBps": round(step_bytes(W.SWEEP[-1], algo)
+                     "bytes_moved_GBps": round(step_bytes(W.SWEEP[-1], algo.split("+")[0])
                                                / W.SWEEP[-1].bytes_per_rank / b / 1e9, 1)}
     cross = {}
-    for x, y in (("ring_step", "tree"), ("halving_doubling", "tree"), ("ring_step", "ring_fused")):
+    for x, y in (("ring_step", "tree"), ("halving_doubling", "tree"), ("ring_step", "ring_fused"),
+                 ("ring_step+graph", "tree+graph")):
         ax, bx = fit[x]["a_us"], fit[x]["b_us_per_MiB"]
         ay, by = fit[y]["a_us"], fit[y]["b_us_per_MiB"]
         cross[f"{x}_vs_{y}_MiB"] = (round((ay - ax) / (bx - by), 3) if bx != by else None)
@@ -339,13 +349,16 @@ def main():
                                      and w.nranks & (w.nranks - 1)):
                 continue
             reps = max(5, min(args.steps // 4, 100))
-            wl, m = time_algo(ar, sets, w, algo, reps, 3)
-            others[algo] = {
-                "us_per_allreduce": round(wl / reps * 1e6, 2),
-                "GBps_algorithmic": round(alg_bytes * reps / wl / 1e9, 2),
-                "GBps_bytes_moved": round(step_bytes(w, algo) * reps / wl / 1e9, 2),
-                "event_us_per_allreduce": round(m * 1e3, 2),
-            }
+            for graph in ((False, True) if algo != "ring_fused" else (False,)):
+                ar.set_graphs(graph, max_bytes_per_rank=ALWAYS_REPLAY)
+                wl, m = time_algo(ar, sets, w, algo, reps, 3)
+                ar.set_graphs(False)
+                others[algo + ("_graph" if graph else "")] = {
+                    "us_per_allreduce": round(wl / reps * 1e6, 2),
+                    "GBps_algorithmic": round(alg_bytes * reps / wl / 1e9, 2),
+                    "GBps_bytes_moved": round(step_bytes(w, algo) * reps / wl / 1e9, 2),
+                    "event_us_per_allreduce": round(m * 1e3, 2),
+                }
         # the two halves on their own (fused kernels): ReduceScatter reads every
         # rank's chunks and writes the owner's (N*K + K bytes); AllGather reads
         # the owners' chunks and writes the other N-1 copies (N*K bytes)

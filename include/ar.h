@@ -23,8 +23,9 @@
  *    device fault surfaces at the caller's next synchronisation of that stream.
  *  - count == 0 and nranks == 1 are successful no-ops (AVG over one rank is
  *    the identity).
- *  - No call allocates device memory: the pointer table travels by value in
- *    the kernel arguments.
+ *  - No call allocates device memory for data: the pointer table travels by
+ *    value in the kernel arguments.  (With ar_set_graphs on, the HIP runtime
+ *    allocates what an instantiated graph needs, once per recorded graph.)
  *  - No C++ exception crosses this interface.  A context is not thread-safe;
  *    use one per host thread / stream.
  *  - ar_last_error(ctx) describes the most recent failure on that context.
@@ -122,6 +123,35 @@ ar_status ar_create(ar_ctx** out, int device, void* stream);
 /* Rebind the context to another stream (hipStream_t, NULL = null stream) of
  * the same device.  Subsequent calls enqueue there. */
 ar_status ar_set_stream(ar_ctx* ctx, void* stream);
+
+/* Graph replay of the multi-launch algorithms (RING_STEP, TREE,
+ * HALVING_DOUBLING, DOUBLE_TREE), for ar_allreduce, ar_reduce_scatter and
+ * ar_allgather.  Each of their steps is a dependent kernel launch, the
+ * one-GPU counterpart of the per-message latency alpha in the pages' cost
+ * model ("AllReduce", compassingai.com, section 4); replaying the recorded
+ * sequence as one graph cuts that per-step cost where it dominates, i.e. for
+ * small messages.
+ * max_bytes_per_rank > 0: a collective of at most that many bytes per rank
+ * (count * element size) is replayed: its first call on a given pointer set
+ * and shape (collective, algo, dtype, op, nranks, count) records the kernel
+ * sequence into a HIP graph on a private stream the library creates, and that
+ * call and every later identical one launch the instantiated graph on the
+ * context's stream.  Larger collectives launch directly.  The same kernels
+ * run in the same order, so results are bitwise those of direct launches.
+ * Up to 64 graphs are kept per context; the least recently used is released
+ * (after its last replay has finished) to make room.  While the context's
+ * stream is itself being captured by the caller, kernels are launched
+ * directly so they land in the caller's graph.
+ * max_bytes_per_rank == 0 (the default) launches everything directly and
+ * releases every recorded graph, waiting for its last replay.  On MI355X,
+ * replay halves a 64-rank per-step ring at 4 KiB per rank and is a few
+ * percent slower than direct launches from about 16 MiB per rank, hence
+ * AR_GRAPHS_MAX_BYTES_DEFAULT.  RING_FUSED and the single-step calls are one
+ * launch and are not affected.  Errors: ctx == NULL -> AR_ERR_INVALID_ARG; a
+ * failed capture or instantiation makes the collective call return
+ * AR_ERR_RUNTIME. */
+#define AR_GRAPHS_MAX_BYTES_DEFAULT ((size_t)8 << 20)
+ar_status ar_set_graphs(ar_ctx* ctx, size_t max_bytes_per_rank);
 
 /* AllReduce in place: every bufs[r][0:count) ends with the reduction of all
  * ranks' inputs.  RING_STEP and RING_FUSED give identical bits; TREE and

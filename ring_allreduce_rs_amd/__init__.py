@@ -18,14 +18,14 @@ from __future__ import annotations
 import ctypes
 
 from ._lib import (  # noqa: F401
-    ALGOS, AR_MAX_RANKS, DTYPES, EXPORTS, LIB_PATH, OPS, ArError, Context, auto_algo,
-    chunk_range, lib, predict_us,
+    ALGOS, AR_GRAPHS_MAX_BYTES_DEFAULT, AR_MAX_RANKS, DTYPES, EXPORTS, LIB_PATH, OPS, ArError,
+    Context, auto_algo, chunk_range, lib, predict_us,
 )
 
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
     "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "dtree_step", "copy_", "chunk_range", "bind",
-    "context", "LIB_PATH", "predict_us", "auto_algo",
+    "context", "LIB_PATH", "predict_us", "auto_algo", "set_graphs",
 ]
 
 _ctx: dict = {}
@@ -76,6 +76,14 @@ def context(device: int = 0) -> Context:
         _ctx[device] = c
     c.set_stream(torch.cuda.current_stream(device).cuda_stream)
     return c
+
+
+def set_graphs(enable: bool = True, device: int = 0,
+               max_bytes_per_rank: int = AR_GRAPHS_MAX_BYTES_DEFAULT) -> None:
+    """Turn graph replay of the multi-launch algorithms on (for collectives of
+    at most ``max_bytes_per_rank`` bytes per rank) or off, for the device's
+    context (see ar_set_graphs)."""
+    context(device).set_graphs(max_bytes_per_rank if enable else 0)
 
 
 def allreduce(tensors, op: str = "sum", algo: str = "ring_fused"):

@@ -14,6 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libar.so")
 
 AR_MAX_RANKS = 64
+AR_GRAPHS_MAX_BYTES_DEFAULT = 8 << 20
 
 AR_OK = 0
 AR_ERR_INVALID_ARG = 1
@@ -29,7 +30,7 @@ ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 # every symbol include/ar.h declares
 EXPORTS = (
-    "ar_create", "ar_set_stream", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
+    "ar_create", "ar_set_stream", "ar_set_graphs", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
     "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
     "ar_dtree_step",
     "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy",
@@ -65,6 +66,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "ar_create": ([ctypes.POINTER(vp), i, vp], i),
         "ar_set_stream": ([vp, vp], i),
+        "ar_set_graphs": ([vp, sz], i),
         "ar_allreduce": ([vp, pp, i, sz, i, i, i], i),
         "ar_reduce_scatter": ([vp, pp, i, sz, i, i, i], i),
         "ar_allgather": ([vp, pp, i, sz, i, i], i),
@@ -144,6 +146,11 @@ class Context:
         if s != self._stream:
             self._check(lib.ar_set_stream(self._h, s or None), "ar_set_stream")
             self._stream = s
+
+    def set_graphs(self, max_bytes_per_rank: int) -> None:
+        """Replay multi-launch collectives of at most this many bytes per rank
+        from recorded HIP graphs; 0 turns replay off (ar_set_graphs)."""
+        self._check(lib.ar_set_graphs(self._h, max_bytes_per_rank), "ar_set_graphs")
 
     def last_error(self) -> str:
         return lib.ar_last_error(self._h).decode()

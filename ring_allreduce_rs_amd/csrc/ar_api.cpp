@@ -31,6 +31,17 @@ struct CheckedSet {
     uint64_t stamp = 0;
 };
 
+// A recorded launch sequence.  `done` is recorded after every replay so the
+// executable graph can be released only once its last replay has finished.
+struct GraphEntry {
+    std::vector<uint64_t> key;
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;
+    uint64_t stamp = 0;
+};
+
+static constexpr size_t kGraphCacheSize = 64;
+
 struct ar_ctx {
     int device = 0;
     hipStream_t stream = nullptr;
@@ -40,6 +51,12 @@ struct ar_ctx {
     // pointers with the runtime costs more than a small message's kernel.
     std::vector<CheckedSet> checked;
     uint64_t clock = 0;
+    // Graph replay of multi-launch collectives (ar_set_graphs): one
+    // instantiated graph per (collective, algorithm, shape, pointer set),
+    // recorded on a private stream and launched on `stream`.
+    size_t graph_max_bytes = 0;   // replay collectives of at most this many bytes per rank
+    hipStream_t capture = nullptr;
+    std::vector<GraphEntry> graph_cache;
 };
 
 static constexpr size_t kCheckedSets = 32;
@@ -256,7 +273,7 @@ ar_status check_buffers(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
     return AR_OK;
 }
 
-ar_status run(ar_ctx* ctx, const arlib::Plan& p, const arlib::RankTable& t) {
+ar_status run(ar_ctx* ctx, hipStream_t stream, const arlib::Plan& p, const arlib::RankTable& t) {
     if (debug_enabled()) {
         arlib::Shape sh{};
         arlib::plan_shape(p, &sh);
@@ -266,7 +283,7 @@ ar_status run(ar_ctx* ctx, const arlib::Plan& p, const arlib::RankTable& t) {
                      (int)p.kind, (int)p.dtype, (int)p.op, p.nranks, p.count, p.step, (int)p.vec,
                      p.mis, sh.blocks, sh.tiles, sh.threads);
     }
-    const hipError_t e = arlib::launch(p, t, ctx->stream);
+    const hipError_t e = arlib::launch(p, t, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(ctx, AR_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
@@ -315,6 +332,191 @@ ar_status check_shape(ar_ctx* ctx, arlib::Kind k, int dtype, int nranks, size_t 
 // The collective entry points share this body.
 enum Coll { COLL_AR, COLL_RS, COLL_AG };
 
+// A validated collective: everything its launch sequence depends on.
+struct Launch {
+    Coll coll;
+    int algo;   // resolved (never AUTO)
+    int dtype;
+    int op;     // AR_SUM for AllGather
+    int nranks;
+    size_t count;
+    bool vec;
+    unsigned mis;
+    arlib::RankTable t;
+};
+
+int launches_of(const Launch& L) {
+    const int lv = log2_exact(L.nranks);
+    const bool rs = L.coll != COLL_AG, ag = L.coll != COLL_RS;
+    switch (L.algo) {
+        case AR_ALGO_RING_FUSED: return 1;
+        case AR_ALGO_TREE: return lv;
+        case AR_ALGO_DOUBLE_TREE: return 2 * lv;
+        case AR_ALGO_HALVING_DOUBLING: return (rs ? lv : 0) + (ag ? lv : 0);
+        default: return (rs ? L.nranks - 1 : 0) + (ag ? L.nranks - 1 : 0);
+    }
+}
+
+// Enqueues the kernels of L on `stream`, in order.
+ar_status enqueue(ar_ctx* ctx, hipStream_t stream, const Launch& L) {
+    ar_status s = AR_OK;
+    auto step = [&](arlib::Kind k, int st) {
+        return run(ctx, stream, make_plan(k, L.dtype, L.op, L.nranks, L.count, st, L.vec, L.mis),
+                   L.t);
+    };
+    const int levels = log2_exact(L.nranks);
+    if (L.algo == AR_ALGO_RING_FUSED) {
+        const arlib::Kind k = L.coll == COLL_AR   ? arlib::KIND_FUSED_AR
+                              : L.coll == COLL_RS ? arlib::KIND_FUSED_RS
+                                                  : arlib::KIND_FUSED_AG;
+        return step(k, 0);
+    }
+    if (L.algo == AR_ALGO_HALVING_DOUBLING) {
+        if (L.coll != COLL_AG)
+            for (int st = 0; st < levels && s == AR_OK; ++st) s = step(arlib::KIND_HD_RS_STEP, st);
+        if (L.coll != COLL_RS)
+            for (int st = 0; st < levels && s == AR_OK; ++st) s = step(arlib::KIND_HD_AG_STEP, st);
+        return s;
+    }
+    if (L.algo == AR_ALGO_DOUBLE_TREE) {
+        for (int st = 0; st < 2 * levels && s == AR_OK; ++st) s = step(arlib::KIND_DT_STEP, st);
+        return s;
+    }
+    if (L.algo == AR_ALGO_TREE) {
+        for (int st = 0; st < levels && s == AR_OK; ++st) s = step(arlib::KIND_TREE_STEP, st);
+        return s;
+    }
+    if (L.coll != COLL_AG)
+        for (int k = 0; k <= L.nranks - 2 && s == AR_OK; ++k) s = step(arlib::KIND_RS_STEP, k);
+    if (L.coll != COLL_RS)
+        for (int k = 0; k <= L.nranks - 2 && s == AR_OK; ++k) s = step(arlib::KIND_AG_STEP, k);
+    return s;
+}
+
+// ------------------------------------------------------------ graph replay
+//
+// A multi-launch collective pays the launch and inter-kernel gap once per
+// step.  With graphs enabled the launch sequence is recorded once on a
+// private stream into a HIP graph (the kernel arguments, pointer table
+// included, are baked in) and later calls of the same collective on the same
+// buffers replay it with one hipGraphLaunch.  Results are identical: the same
+// kernels run in the same order.
+
+std::vector<uint64_t> key_of(const Launch& L) {
+    std::vector<uint64_t> k;
+    k.reserve(8 + (size_t)L.nranks);
+    k.push_back((uint64_t)L.coll);
+    k.push_back((uint64_t)L.algo);
+    k.push_back((uint64_t)L.dtype);
+    k.push_back((uint64_t)L.op);
+    k.push_back((uint64_t)L.nranks);
+    k.push_back((uint64_t)L.count);
+    k.push_back((uint64_t)L.vec);
+    k.push_back((uint64_t)L.mis);
+    for (int r = 0; r < L.nranks; ++r) k.push_back(reinterpret_cast<uint64_t>(L.t.p[r]));
+    return k;
+}
+
+// Waits for the entry's last replay, then frees it.
+void release(GraphEntry& e) {
+    if (e.done) {
+        (void)hipEventSynchronize(e.done);
+        (void)hipEventDestroy(e.done);
+    }
+    if (e.exec) (void)hipGraphExecDestroy(e.exec);
+    (void)hipGetLastError();
+    e.done = nullptr;
+    e.exec = nullptr;
+}
+
+ar_status record(ar_ctx* ctx, const Launch& L, GraphEntry* out) {
+    if (!ctx->capture &&
+        hipStreamCreateWithFlags(&ctx->capture, hipStreamNonBlocking) != hipSuccess) {
+        (void)hipGetLastError();
+        ctx->capture = nullptr;
+        return fail(ctx, AR_ERR_RUNTIME, "cannot create the capture stream");
+    }
+    hipError_t e = hipStreamBeginCapture(ctx->capture, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_RUNTIME, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+    }
+    const ar_status s = enqueue(ctx, ctx->capture, L);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(ctx->capture, &graph);
+    if (s != AR_OK || e != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        (void)hipGetLastError();
+        if (s != AR_OK) return s;
+        return fail(ctx, AR_ERR_RUNTIME, "hipStreamEndCapture: %s", hipGetErrorString(e));
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess || !exec) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_RUNTIME, "hipGraphInstantiate: %s", hipGetErrorString(e));
+    }
+    hipEvent_t done = nullptr;
+    if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipGraphExecDestroy(exec);
+        return fail(ctx, AR_ERR_RUNTIME, "cannot create a graph event");
+    }
+    out->key = key_of(L);
+    out->exec = exec;
+    out->done = done;
+    return AR_OK;
+}
+
+ar_status replay(ar_ctx* ctx, const Launch& L) {
+    // A stream that is itself being captured (the caller builds its own
+    // graph) gets the kernels directly, so they land in the caller's graph.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(ctx->stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return enqueue(ctx, ctx->stream, L);
+    }
+    if (cs != hipStreamCaptureStatusNone) return enqueue(ctx, ctx->stream, L);
+
+    const std::vector<uint64_t> key = key_of(L);
+    GraphEntry* hit = nullptr;
+    for (GraphEntry& e : ctx->graph_cache)
+        if (e.key == key) {
+            hit = &e;
+            break;
+        }
+    if (!hit) {
+        GraphEntry fresh;
+        const ar_status s = record(ctx, L, &fresh);
+        if (s != AR_OK) return s;
+        if (ctx->graph_cache.size() < kGraphCacheSize) {
+            ctx->graph_cache.push_back(std::move(fresh));
+            hit = &ctx->graph_cache.back();
+        } else {
+            size_t oldest = 0;
+            for (size_t i = 1; i < ctx->graph_cache.size(); ++i)
+                if (ctx->graph_cache[i].stamp < ctx->graph_cache[oldest].stamp) oldest = i;
+            release(ctx->graph_cache[oldest]);
+            ctx->graph_cache[oldest] = std::move(fresh);
+            hit = &ctx->graph_cache[oldest];
+        }
+    }
+    hit->stamp = ++ctx->clock;
+    hipError_t e = hipGraphLaunch(hit->exec, ctx->stream);
+    if (e == hipSuccess) e = hipEventRecord(hit->done, ctx->stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_RUNTIME, "hipGraphLaunch: %s", hipGetErrorString(e));
+    }
+    return AR_OK;
+}
+
+void clear_graphs(ar_ctx* ctx) {
+    for (GraphEntry& e : ctx->graph_cache) release(e);
+    ctx->graph_cache.clear();
+}
+
 ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size_t count,
                      int dtype, int op, int algo) {
     if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
@@ -354,61 +556,11 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
 
         DeviceGuard g(ctx->device);
         if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
-        const arlib::RankTable t = table_of(bufs, nranks);
-        const int o = coll == COLL_AG ? AR_SUM : op;
-        if (algo == AR_ALGO_RING_FUSED) {
-            const arlib::Kind k = coll == COLL_AR   ? arlib::KIND_FUSED_AR
-                                  : coll == COLL_RS ? arlib::KIND_FUSED_RS
-                                                    : arlib::KIND_FUSED_AG;
-            return run(ctx, make_plan(k, dtype, o, nranks, count, 0, vec, mis), t);
-        }
-        if (algo == AR_ALGO_HALVING_DOUBLING) {
-            const int levels = log2_exact(nranks);
-            if (coll != COLL_AG) {
-                for (int st = 0; st < levels; ++st) {
-                    s = run(ctx, make_plan(arlib::KIND_HD_RS_STEP, dtype, o, nranks, count, st,
-                                           vec, mis), t);
-                    if (s != AR_OK) return s;
-                }
-            }
-            if (coll != COLL_RS) {
-                for (int st = 0; st < levels; ++st) {
-                    s = run(ctx, make_plan(arlib::KIND_HD_AG_STEP, dtype, o, nranks, count, st,
-                                           vec, mis), t);
-                    if (s != AR_OK) return s;
-                }
-            }
-            return AR_OK;
-        }
-        if (algo == AR_ALGO_DOUBLE_TREE) {
-            for (int st = 0; st < 2 * log2_exact(nranks); ++st) {
-                s = run(ctx, make_plan(arlib::KIND_DT_STEP, dtype, o, nranks, count, st, vec, mis),
-                        t);
-                if (s != AR_OK) return s;
-            }
-            return AR_OK;
-        }
-        if (algo == AR_ALGO_TREE) {
-            for (int st = 0; (1 << st) < nranks; ++st) {
-                s = run(ctx, make_plan(arlib::KIND_TREE_STEP, dtype, o, nranks, count, st, vec, mis),
-                        t);
-                if (s != AR_OK) return s;
-            }
-            return AR_OK;
-        }
-        if (coll != COLL_AG) {
-            for (int k = 0; k <= nranks - 2; ++k) {
-                s = run(ctx, make_plan(arlib::KIND_RS_STEP, dtype, o, nranks, count, k, vec, mis), t);
-                if (s != AR_OK) return s;
-            }
-        }
-        if (coll != COLL_RS) {
-            for (int k = 0; k <= nranks - 2; ++k) {
-                s = run(ctx, make_plan(arlib::KIND_AG_STEP, dtype, o, nranks, count, k, vec, mis), t);
-                if (s != AR_OK) return s;
-            }
-        }
-        return AR_OK;
+        const Launch L{coll, algo, dtype, coll == COLL_AG ? AR_SUM : op, nranks, count, vec, mis,
+                       table_of(bufs, nranks)};
+        if (count * elem_bytes((ar_dtype)dtype) <= ctx->graph_max_bytes && launches_of(L) > 1)
+            return replay(ctx, L);
+        return enqueue(ctx, ctx->stream, L);
     } catch (const std::bad_alloc&) {
         return fail(ctx, AR_ERR_NO_MEMORY, "host allocation failed");
     } catch (...) {
@@ -444,7 +596,7 @@ ar_status single_step(ar_ctx* ctx, arlib::Kind kind, void* const* bufs, int nran
         DeviceGuard g(ctx->device);
         if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
         const int o = (kind == arlib::KIND_AG_STEP || kind == arlib::KIND_HD_AG_STEP) ? AR_SUM : op;
-        return run(ctx, make_plan(kind, dtype, o, nranks, count, step, vec, mis),
+        return run(ctx, ctx->stream, make_plan(kind, dtype, o, nranks, count, step, vec, mis),
                    table_of(bufs, nranks));
     } catch (...) {
         return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
@@ -477,6 +629,16 @@ ar_status ar_create(ar_ctx** out, int device, void* stream) {
 ar_status ar_set_stream(ar_ctx* ctx, void* stream) {
     if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
     ctx->stream = reinterpret_cast<hipStream_t>(stream);
+    return AR_OK;
+}
+
+ar_status ar_set_graphs(ar_ctx* ctx, size_t max_bytes_per_rank) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->graph_max_bytes = max_bytes_per_rank;
+    if (max_bytes_per_rank == 0) {
+        DeviceGuard g(ctx->device);
+        clear_graphs(ctx);
+    }
     return AR_OK;
 }
 
@@ -595,6 +757,13 @@ const char* ar_last_error(const ar_ctx* ctx) {
 }
 
 ar_status ar_destroy(ar_ctx* ctx) {
+    if (!ctx) return AR_OK;
+    if (!ctx->graph_cache.empty() || ctx->capture) {
+        DeviceGuard g(ctx->device);
+        clear_graphs(ctx);
+        if (ctx->capture) (void)hipStreamDestroy(ctx->capture);
+        (void)hipGetLastError();
+    }
     delete ctx;
     return AR_OK;
 }
