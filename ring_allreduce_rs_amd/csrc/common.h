@@ -37,6 +37,9 @@ constexpr int kBatch = 8;           // ranks of loads issued before they are fol
 #ifndef AR_FUSED_FORCE_CFG
 #define AR_FUSED_FORCE_CFG -1
 #endif
+#ifndef AR_FUSED_TINY_MAX_CHUNK_BYTES
+#define AR_FUSED_TINY_MAX_CHUNK_BYTES 4096u
+#endif
 #ifndef AR_FUSED_DEEP_MAX_CHUNK_BYTES
 #define AR_FUSED_DEEP_MAX_CHUNK_BYTES (256u << 10)
 #endif
@@ -44,16 +47,27 @@ constexpr int kBatch = 8;           // ranks of loads issued before they are fol
 struct FusedWide {
     static constexpr int U = kFusedUnroll;
     static constexpr int B = kBatch;
+    static constexpr bool kWrapLoads = false;
 };
 struct FusedDeep {
     static constexpr int U = 1;
     static constexpr int B = 32;
+    static constexpr bool kWrapLoads = false;
 };
 struct FusedMid {
     static constexpr int U = 2;
     static constexpr int B = 16;
+    static constexpr bool kWrapLoads = false;
 };
-enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_MID = 2 };
+// TINY: element-wise units with every rank's load in flight at once (one
+// memory round trip for up to 64 ranks instead of DEEP's two); for chunks so
+// small that latency, not bandwidth, sets the time.
+struct FusedTiny {
+    static constexpr int U = 1;
+    static constexpr int B = AR_MAX_RANKS;
+    static constexpr bool kWrapLoads = true;
+};
+enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_MID = 2, CFG_TINY = 3 };
 constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
 // Streaming (non-temporal) loads and stores.  The fused kernel touches every
 // byte once, so caching it only evicts useful lines: on MI355X 8 x 25 MiB went

@@ -12,21 +12,30 @@ int fused_variant(const Plan& p) {
     // 16 x 1 GiB: 6.9 ms vs 7.7 ms); DEEP for 64 ranks (64 x 64 MiB: 1.60 ms
     // vs 1.88 ms) and for bf16, whose per-hop rounding makes the fold
     // ALU-heavier and favours the higher occupancy (8 x 2 GiB: 5.97 ms vs
-    // 6.39 ms); small chunks are latency-bound and also favour DEEP.
+    // 6.39 ms); small chunks are latency-bound and also favour DEEP.  Beyond
+    // DEEP's 32 ranks of loads per batch, chunks of at most 4 KiB take TINY
+    // (every rank's element load in flight at once: 64 x 4 KiB 8.3 -> 5.0 us,
+    // 64 x 64 KiB 8.1 -> 5.5 us); at 16 KiB chunks its 4-byte loads lose
+    // (64 x 1 MiB: 23 -> 32 us).
+    const size_t per = ceil_div(p.count, (size_t)p.nranks) * (size_t)elem_bytes(p.dtype);
+    if (p.nranks > FusedDeep::B && per <= (size_t)AR_FUSED_TINY_MAX_CHUNK_BYTES) return CFG_TINY;
     if (p.dtype == AR_BFLOAT16 || p.nranks > 16) return CFG_DEEP;
     if (p.nranks <= kBatch) return CFG_WIDE;
-    const size_t per = ceil_div(p.count, (size_t)p.nranks) * (size_t)elem_bytes(p.dtype);
     return per <= (size_t)AR_FUSED_DEEP_MAX_CHUNK_BYTES ? CFG_DEEP : CFG_WIDE;
 }
 
 int fused_units_per_lane(int cfg) {
-    return cfg == CFG_DEEP ? FusedDeep::U : cfg == CFG_MID ? FusedMid::U : FusedWide::U;
+    return cfg == CFG_DEEP   ? FusedDeep::U
+           : cfg == CFG_MID  ? FusedMid::U
+           : cfg == CFG_TINY ? FusedTiny::U
+                             : FusedWide::U;
 }
 
 bool plan_shape(const Plan& p, Shape* out) {
     const size_t eb = (size_t)elem_bytes(p.dtype);
-    const size_t epu = p.vec ? 16 / eb : 1;
     const bool fused = p.kind == KIND_FUSED_AR || p.kind == KIND_FUSED_RS || p.kind == KIND_FUSED_AG;
+    // the TINY fused shape moves elements, not 16-byte units
+    const size_t epu = p.vec && !(fused && fused_variant(p) == CFG_TINY) ? 16 / eb : 1;
     const size_t threads = fused ? kFusedThreads : kThreads;
     const size_t per_tile =
         threads * (fused ? (size_t)fused_units_per_lane(fused_variant(p)) : (size_t)kUnroll);

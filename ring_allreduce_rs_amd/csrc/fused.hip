@@ -65,7 +65,10 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
             int rr = r;
 #pragma unroll
             for (int j = 0; j < kB; ++j) {
-                if (j0 + j < n) {
+                // kWrapLoads: issue every slot's load (ranks wrap mod n, so the
+                // addresses stay valid) and keep only the first n in the fold;
+                // a uniform guard here lets the compiler serialise the loads
+                if (CFG::kWrapLoads || j0 + j < n) {
                     const char* src = rank_ptr(a, rr);
 #pragma unroll
                     for (int u = 0; u < U; ++u)
@@ -73,6 +76,8 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
                     rr = (rr + 1 == n) ? 0 : rr + 1;
                 }
             }
+            // keep the adds behind the whole batch: one memory round trip
+            if constexpr (CFG::kWrapLoads) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kB; ++j) {
                 if (j0 + j < n) {
@@ -137,7 +142,10 @@ static void launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStream_t 
     const dim3 block(kFusedThreads);
     const int cfg = fused_variant(p);
     const bool n8 = AR_SPECIALIZE_N && VEC && p.nranks == 8;
-    if (cfg == CFG_DEEP) {
+    if (cfg == CFG_TINY) {
+        // element-wise units whatever the alignment (the grid was sized so)
+        hipLaunchKernelGGL((k_fused<Op, MODE, false, 0, FusedTiny>), grid, block, 0, s, a);
+    } else if (cfg == CFG_DEEP) {
         // the runtime-N loop measured faster than the 8-rank unrolled one here
         hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep>), grid, block, 0, s, a);
     } else if (cfg == CFG_MID) {

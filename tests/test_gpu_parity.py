@@ -269,3 +269,28 @@ def test_every_double_tree_step_matches_oracle_snapshot(dtype, op, n, count):
         torch.cuda.synchronize()
         for r in range(n):
             assert_bits_equal(to_np(ts[r]), snaps[s][r], f"dtree step {s} rank {r}")
+
+
+# 33..64 ranks with chunks of at most 4 KiB take the fused kernel's
+# element-wise all-loads-in-flight shape; 4100-byte chunks take the 16-byte
+# one.  Both sides of that boundary, ragged counts and counts below N.
+MANY_RANKS = [(33, 1), (33, 500), (40, 2050), (48, 3001), (64, 1), (64, 63), (64, 4101),
+              (64, 65536), (64, 65600)]
+
+
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("n,count", MANY_RANKS)
+def test_fused_many_ranks_small_chunks(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n * 104729 + count)
+    want = oracle.simulate_ring_allreduce(xs, dtype, op).state
+    ts = to_gpu(xs, dtype)
+    ar.allreduce(ts, op=op, algo="ring_fused")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), want[r], f"fused {dtype} {op} n={n} count={count} rank {r}")
+    ts = to_gpu(xs, dtype)
+    ar.reduce_scatter(ts, op=op, algo="ring_fused")
+    torch.cuda.synchronize()
+    for r, (lo, ln) in enumerate(oracle.chunk_layout(count, n)):
+        assert_bits_equal(to_np(ts[r])[lo:lo + ln], want[r][lo:lo + ln],
+                          f"fused RS {dtype} {op} n={n} count={count} rank {r}")
