@@ -45,9 +45,18 @@ extern "C" {
 
 #define AR_MAX_RANKS 64
 
+/* Under C++ the enums below have int as their fixed underlying type, so any
+ * int a C caller passes (including out-of-range values, which the library
+ * rejects) is a valid value of the enum type; the ABI is the same as C's. */
+#ifdef __cplusplus
+#define AR_ENUM_INT : int
+#else
+#define AR_ENUM_INT
+#endif
+
 typedef struct ar_ctx ar_ctx;
 
-typedef enum ar_status {
+typedef enum ar_status AR_ENUM_INT {
     AR_OK = 0,
     AR_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum, overlap, step index */
     AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, TREE / HALVING_DOUBLING /
@@ -57,7 +66,7 @@ typedef enum ar_status {
     AR_ERR_NO_MEMORY = 4      /* host allocation of the context failed */
 } ar_status;
 
-typedef enum ar_dtype { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BFLOAT16 = 2 } ar_dtype;
+typedef enum ar_dtype AR_ENUM_INT { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BFLOAT16 = 2 } ar_dtype;
 
 /* Reduction operator.  Per-hop arithmetic: int32 SUM wraps (two's complement);
  * fp32 SUM is one binary32 round-to-nearest-even add per hop; bf16 SUM adds in
@@ -67,7 +76,7 @@ typedef enum ar_dtype { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BFLOAT16 = 2 } ar_dtype
  * (DDP's divide by world size: pwwt.cn page, sections 3.1-3.2): fp32 correctly
  * rounded, bf16 rounded from the fp32 quotient.  AVG on int32 is
  * AR_ERR_UNSUPPORTED. */
-typedef enum ar_op { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
+typedef enum ar_op AR_ENUM_INT { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
 
 /* Algorithm.
  *  RING_STEP  -- the ring as the pages lay it out: N-1 ReduceScatter steps then
@@ -105,7 +114,7 @@ typedef enum ar_op { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
  *                sections 4-5; xdnf.cn page, section 4.3).  On one GPU the fused
  *                pass needs one launch and the fewest bytes, so the model picks
  *                RING_FUSED at every size measured. */
-typedef enum ar_algo {
+typedef enum ar_algo AR_ENUM_INT {
     AR_ALGO_RING_STEP = 0,
     AR_ALGO_RING_FUSED = 1,
     AR_ALGO_TREE = 2,

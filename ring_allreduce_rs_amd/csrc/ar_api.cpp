@@ -319,16 +319,6 @@ ar_status check_op(ar_ctx* ctx, int dtype, int op) {
     return AR_OK;
 }
 
-ar_status check_shape(ar_ctx* ctx, arlib::Kind k, int dtype, int nranks, size_t count,
-                      bool vec, int step = 0) {
-    arlib::Plan p = make_plan(k, dtype, AR_SUM, nranks, count, step, vec, 0);
-    arlib::Shape sh;
-    if (!arlib::plan_shape(p, &sh))
-        return fail(ctx, AR_ERR_INVALID_ARG, "count %zu needs more blocks than one grid holds",
-                    count);
-    return AR_OK;
-}
-
 // The collective entry points share this body.
 enum Coll { COLL_AR, COLL_RS, COLL_AG };
 
@@ -345,52 +335,56 @@ struct Launch {
     arlib::RankTable t;
 };
 
-int launches_of(const Launch& L) {
-    const int lv = log2_exact(L.nranks);
+// The kernels of L, in launch order.
+std::vector<arlib::Plan> plans_of(const Launch& L) {
+    std::vector<arlib::Plan> ps;
+    auto add = [&](arlib::Kind k, int st) {
+        ps.push_back(make_plan(k, L.dtype, L.op, L.nranks, L.count, st, L.vec, L.mis));
+    };
+    const int levels = log2_exact(L.nranks);
     const bool rs = L.coll != COLL_AG, ag = L.coll != COLL_RS;
     switch (L.algo) {
-        case AR_ALGO_RING_FUSED: return 1;
-        case AR_ALGO_TREE: return lv;
-        case AR_ALGO_DOUBLE_TREE: return 2 * lv;
-        case AR_ALGO_HALVING_DOUBLING: return (rs ? lv : 0) + (ag ? lv : 0);
-        default: return (rs ? L.nranks - 1 : 0) + (ag ? L.nranks - 1 : 0);
+        case AR_ALGO_RING_FUSED:
+            add(L.coll == COLL_AR   ? arlib::KIND_FUSED_AR
+                : L.coll == COLL_RS ? arlib::KIND_FUSED_RS
+                                    : arlib::KIND_FUSED_AG, 0);
+            break;
+        case AR_ALGO_HALVING_DOUBLING:
+            if (rs) for (int st = 0; st < levels; ++st) add(arlib::KIND_HD_RS_STEP, st);
+            if (ag) for (int st = 0; st < levels; ++st) add(arlib::KIND_HD_AG_STEP, st);
+            break;
+        case AR_ALGO_DOUBLE_TREE:
+            for (int st = 0; st < 2 * levels; ++st) add(arlib::KIND_DT_STEP, st);
+            break;
+        case AR_ALGO_TREE:
+            for (int st = 0; st < levels; ++st) add(arlib::KIND_TREE_STEP, st);
+            break;
+        default:
+            if (rs) for (int k = 0; k <= L.nranks - 2; ++k) add(arlib::KIND_RS_STEP, k);
+            if (ag) for (int k = 0; k <= L.nranks - 2; ++k) add(arlib::KIND_AG_STEP, k);
+            break;
     }
+    return ps;
+}
+
+// Every kernel of L must fit one grid; checked before anything is launched.
+ar_status check_shapes(ar_ctx* ctx, const std::vector<arlib::Plan>& ps) {
+    for (const arlib::Plan& p : ps) {
+        arlib::Shape sh;
+        if (!arlib::plan_shape(p, &sh))
+            return fail(ctx, AR_ERR_INVALID_ARG, "count %zu needs more blocks than one grid holds",
+                        p.count);
+    }
+    return AR_OK;
 }
 
 // Enqueues the kernels of L on `stream`, in order.
 ar_status enqueue(ar_ctx* ctx, hipStream_t stream, const Launch& L) {
-    ar_status s = AR_OK;
-    auto step = [&](arlib::Kind k, int st) {
-        return run(ctx, stream, make_plan(k, L.dtype, L.op, L.nranks, L.count, st, L.vec, L.mis),
-                   L.t);
-    };
-    const int levels = log2_exact(L.nranks);
-    if (L.algo == AR_ALGO_RING_FUSED) {
-        const arlib::Kind k = L.coll == COLL_AR   ? arlib::KIND_FUSED_AR
-                              : L.coll == COLL_RS ? arlib::KIND_FUSED_RS
-                                                  : arlib::KIND_FUSED_AG;
-        return step(k, 0);
+    for (const arlib::Plan& p : plans_of(L)) {
+        const ar_status s = run(ctx, stream, p, L.t);
+        if (s != AR_OK) return s;
     }
-    if (L.algo == AR_ALGO_HALVING_DOUBLING) {
-        if (L.coll != COLL_AG)
-            for (int st = 0; st < levels && s == AR_OK; ++st) s = step(arlib::KIND_HD_RS_STEP, st);
-        if (L.coll != COLL_RS)
-            for (int st = 0; st < levels && s == AR_OK; ++st) s = step(arlib::KIND_HD_AG_STEP, st);
-        return s;
-    }
-    if (L.algo == AR_ALGO_DOUBLE_TREE) {
-        for (int st = 0; st < 2 * levels && s == AR_OK; ++st) s = step(arlib::KIND_DT_STEP, st);
-        return s;
-    }
-    if (L.algo == AR_ALGO_TREE) {
-        for (int st = 0; st < levels && s == AR_OK; ++st) s = step(arlib::KIND_TREE_STEP, st);
-        return s;
-    }
-    if (L.coll != COLL_AG)
-        for (int k = 0; k <= L.nranks - 2 && s == AR_OK; ++k) s = step(arlib::KIND_RS_STEP, k);
-    if (L.coll != COLL_RS)
-        for (int k = 0; k <= L.nranks - 2 && s == AR_OK; ++k) s = step(arlib::KIND_AG_STEP, k);
-    return s;
+    return AR_OK;
 }
 
 // ------------------------------------------------------------ graph replay
@@ -546,19 +540,15 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
             return fail(ctx, AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two nranks, got %d",
                         algo, nranks);
         if (count == 0 || nranks == 1) return AR_OK;
-        const arlib::Kind probe = algo == AR_ALGO_TREE ? arlib::KIND_TREE_STEP
-                                  : algo == AR_ALGO_HALVING_DOUBLING ? arlib::KIND_HD_AG_STEP
-                                  : algo == AR_ALGO_DOUBLE_TREE ? arlib::KIND_DT_STEP
-                                                                : arlib::KIND_RS_STEP;
-        s = check_shape(ctx, probe, dtype, nranks, count, vec,
-                        algo == AR_ALGO_HALVING_DOUBLING ? log2_exact(nranks) - 1 : 0);
+        const Launch L{coll, algo, dtype, coll == COLL_AG ? AR_SUM : op, nranks, count, vec, mis,
+                       table_of(bufs, nranks)};
+        const std::vector<arlib::Plan> plans = plans_of(L);
+        s = check_shapes(ctx, plans);
         if (s != AR_OK) return s;
 
         DeviceGuard g(ctx->device);
         if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
-        const Launch L{coll, algo, dtype, coll == COLL_AG ? AR_SUM : op, nranks, count, vec, mis,
-                       table_of(bufs, nranks)};
-        if (count * elem_bytes((ar_dtype)dtype) <= ctx->graph_max_bytes && launches_of(L) > 1)
+        if (count * elem_bytes((ar_dtype)dtype) <= ctx->graph_max_bytes && plans.size() > 1)
             return replay(ctx, L);
         return enqueue(ctx, ctx->stream, L);
     } catch (const std::bad_alloc&) {
@@ -591,13 +581,13 @@ ar_status single_step(ar_ctx* ctx, arlib::Kind kind, void* const* bufs, int nran
         if (step < 0 || step >= nsteps)
             return fail(ctx, AR_ERR_INVALID_ARG, "step %d outside [0, %d)", step, nsteps);
         if (count == 0) return AR_OK;
-        s = check_shape(ctx, kind, dtype, nranks, count, vec, step);
+        const int o = (kind == arlib::KIND_AG_STEP || kind == arlib::KIND_HD_AG_STEP) ? AR_SUM : op;
+        const arlib::Plan p = make_plan(kind, dtype, o, nranks, count, step, vec, mis);
+        s = check_shapes(ctx, {p});
         if (s != AR_OK) return s;
         DeviceGuard g(ctx->device);
         if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
-        const int o = (kind == arlib::KIND_AG_STEP || kind == arlib::KIND_HD_AG_STEP) ? AR_SUM : op;
-        return run(ctx, ctx->stream, make_plan(kind, dtype, o, nranks, count, step, vec, mis),
-                   table_of(bufs, nranks));
+        return run(ctx, ctx->stream, p, table_of(bufs, nranks));
     } catch (...) {
         return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
     }

@@ -1,0 +1,471 @@
+// driver.cpp -- runs the library's host code against the fake HIP runtime
+// (fake_hip.cpp) under AddressSanitizer / UndefinedBehaviorSanitizer.  Test
+// infrastructure only: prints "ALL OK" and exits 0 when every check passes.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <random>
+#include <vector>
+
+#include "ar.h"
+#include "fake_hip.h"
+
+namespace {
+
+int g_fail = 0;
+#define CHECK(c, ...)                                                      \
+    do {                                                                   \
+        if (!(c)) {                                                        \
+            std::fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__);      \
+            std::fprintf(stderr, __VA_ARGS__);                             \
+            std::fprintf(stderr, "\n");                                    \
+            ++g_fail;                                                      \
+        }                                                                  \
+    } while (0)
+
+// Rank r's fake buffer lives at kBase + r * kStride; nothing is dereferenced.
+constexpr uintptr_t kBase = uintptr_t(1) << 44;
+constexpr uintptr_t kStride = uintptr_t(1) << 43;   // 8 TiB per rank
+constexpr int kMaxN = AR_MAX_RANKS;
+
+void* rank_addr(int r, size_t byte_shift) {
+    return reinterpret_cast<void*>(kBase + (uintptr_t)r * kStride + byte_shift);
+}
+
+size_t eb_of(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
+bool pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+int log2i(int n) {
+    int l = 0;
+    while ((1 << l) < n) ++l;
+    return l;
+}
+
+// ----------------------------------------------------------- chunk layout
+void check_chunk_range() {
+    const size_t counts[] = {0, 1, 2, 3, 37, 1000003, (size_t(1) << 40) + 3, SIZE_MAX / 8};
+    for (int n = 1; n <= kMaxN; ++n) {
+        for (size_t count : counts) {
+            const size_t per = count / (size_t)n + (count % (size_t)n ? 1 : 0);
+            size_t next = 0, total = 0;
+            for (int c = 0; c < n; ++c) {
+                size_t off = 0, len = 0;
+                CHECK(ar_chunk_range(count, n, c, &off, &len) == AR_OK, "chunk_range n=%d c=%d", n, c);
+                const size_t lo = (size_t)c * per < count ? (size_t)c * per : count;
+                CHECK(off == lo, "chunk offset n=%d count=%zu c=%d: %zu vs %zu", n, count, c, off, lo);
+                CHECK(off == next, "chunks not contiguous n=%d count=%zu c=%d", n, count, c);
+                CHECK(len <= per, "chunk longer than L");
+                next = off + len;
+                total += len;
+            }
+            CHECK(total == count, "chunks do not cover count=%zu n=%d", count, n);
+        }
+        size_t o, l;
+        CHECK(ar_chunk_range(10, n, -1, &o, &l) == AR_ERR_INVALID_ARG, "chunk -1");
+        CHECK(ar_chunk_range(10, n, n, &o, &l) == AR_ERR_INVALID_ARG, "chunk n");
+        CHECK(ar_chunk_range(10, n, 0, nullptr, &l) == AR_ERR_INVALID_ARG, "null offset");
+    }
+    size_t o, l;
+    CHECK(ar_chunk_range(10, 0, 0, &o, &l) == AR_ERR_INVALID_ARG, "nranks 0");
+    CHECK(ar_chunk_range(10, kMaxN + 1, 0, &o, &l) == AR_ERR_INVALID_ARG, "nranks 65");
+}
+
+// ------------------------------------------------------------- cost model
+void check_cost_model() {
+    const ar_algo algos[] = {AR_ALGO_RING_STEP, AR_ALGO_RING_FUSED, AR_ALGO_TREE,
+                             AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE};
+    const ar_dtype dts[] = {AR_INT32, AR_FLOAT32, AR_BFLOAT16};
+    for (int n = 1; n <= kMaxN; ++n)
+        for (ar_dtype dt : dts)
+            for (int lg = 0; lg <= 40; lg += 5) {
+                const size_t count = size_t(1) << lg;
+                double best = 1e300;
+                ar_algo best_algo = AR_ALGO_RING_FUSED;
+                for (ar_algo a : algos) {
+                    double us = -1;
+                    const ar_status st = ar_predict_us(a, n, count, dt, &us);
+                    const bool needs_pow2 = a == AR_ALGO_TREE || a == AR_ALGO_HALVING_DOUBLING ||
+                                            a == AR_ALGO_DOUBLE_TREE;
+                    if (needs_pow2 && !pow2(n)) {
+                        CHECK(st == AR_ERR_UNSUPPORTED, "predict needs pow2");
+                        continue;
+                    }
+                    CHECK(st == AR_OK && std::isfinite(us) && us > 0, "predict n=%d lg=%d", n, lg);
+                    if (us < best) {
+                        best = us;
+                        best_algo = a;
+                    }
+                }
+                ar_algo got;
+                CHECK(ar_auto_algo(n, count, dt, &got) == AR_OK, "auto_algo");
+                double got_us = 0;
+                (void)ar_predict_us(got, n, count, dt, &got_us);
+                CHECK(got_us <= best * (1 + 1e-12), "AUTO is not the argmin n=%d lg=%d (%d vs %d)",
+                      n, lg, (int)got, (int)best_algo);
+            }
+    double us;
+    CHECK(ar_predict_us(AR_ALGO_AUTO, 8, 8, AR_FLOAT32, &us) == AR_ERR_INVALID_ARG, "AUTO predict");
+    CHECK(ar_predict_us(AR_ALGO_RING_STEP, 8, 8, AR_FLOAT32, nullptr) == AR_ERR_INVALID_ARG, "null");
+    CHECK(ar_predict_us((ar_algo)99, 8, 8, AR_FLOAT32, &us) == AR_ERR_INVALID_ARG, "bad algo");
+}
+
+// ------------------------------------------------------------ validation
+void check_validation(ar_ctx* ctx) {
+    fake_clear_executed();
+    const long before = fake_counters().kernel_launches;
+    void* bufs[kMaxN];
+    for (int r = 0; r < kMaxN; ++r) bufs[r] = rank_addr(r, 0);
+    auto rejected = [&](ar_status st, ar_status want, const char* what) {
+        CHECK(st == want, "%s: got %d want %d (%s)", what, (int)st, (int)want, ar_last_error(ctx));
+        CHECK(std::strlen(ar_last_error(ctx)) > 0, "%s: empty last_error", what);
+    };
+    rejected(ar_allreduce(ctx, nullptr, 4, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "NULL bufs");
+    rejected(ar_allreduce(ctx, bufs, 0, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "nranks 0");
+    rejected(ar_allreduce(ctx, bufs, kMaxN + 1, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "nranks 65");
+    rejected(ar_allreduce(ctx, bufs, 4, 16, (ar_dtype)7, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "bad dtype");
+    rejected(ar_allreduce(ctx, bufs, 4, 16, AR_FLOAT32, (ar_op)5, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "bad op");
+    rejected(ar_allreduce(ctx, bufs, 4, 16, AR_FLOAT32, AR_SUM, (ar_algo)9), AR_ERR_INVALID_ARG,
+             "bad algo");
+    rejected(ar_allreduce(ctx, bufs, 4, 16, AR_INT32, AR_AVG, AR_ALGO_RING_FUSED),
+             AR_ERR_UNSUPPORTED, "int32 AVG");
+    rejected(ar_allreduce(ctx, bufs, 6, 16, AR_FLOAT32, AR_SUM, AR_ALGO_TREE), AR_ERR_UNSUPPORTED,
+             "tree on 6 ranks");
+    rejected(ar_reduce_scatter(ctx, bufs, 8, 16, AR_FLOAT32, AR_SUM, AR_ALGO_DOUBLE_TREE),
+             AR_ERR_UNSUPPORTED, "double tree RS");
+    rejected(ar_allgather(ctx, bufs, 8, 16, AR_FLOAT32, AR_ALGO_TREE), AR_ERR_UNSUPPORTED,
+             "tree AG");
+    rejected(ar_allreduce(ctx, bufs, 4, SIZE_MAX / 2, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "size overflow");
+
+    void* bad[4] = {bufs[0], bufs[1], nullptr, bufs[3]};
+    rejected(ar_allreduce(ctx, bad, 4, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "NULL rank");
+    void* mis[4] = {bufs[0], rank_addr(1, 2), bufs[2], bufs[3]};
+    rejected(ar_allreduce(ctx, mis, 4, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "misaligned fp32");
+    void* dup[4] = {bufs[0], bufs[1], bufs[1], bufs[3]};
+    rejected(ar_allreduce(ctx, dup, 4, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "overlap");
+    void* near[2] = {bufs[0], rank_addr(0, 60)};
+    rejected(ar_allreduce(ctx, near, 2, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "partial overlap");
+    void* host[2] = {bufs[0], reinterpret_cast<void*>(uintptr_t(0x1000))};
+    rejected(ar_allreduce(ctx, host, 2, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "unregistered pointer");
+    void* past[2] = {bufs[0], rank_addr(1, kStride - 32)};
+    rejected(ar_allreduce(ctx, past, 2, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "runs past its allocation");
+    void* other[2] = {bufs[0], reinterpret_cast<void*>(kBase - kStride)};   // device 1 range
+    rejected(ar_allreduce(ctx, other, 2, 16, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED),
+             AR_ERR_INVALID_ARG, "other device");
+    rejected(ar_ring_rs_step(ctx, bufs, 4, 16, AR_FLOAT32, AR_SUM, 3), AR_ERR_INVALID_ARG,
+             "RS step 3 of 4 ranks");
+    rejected(ar_ring_ag_step(ctx, bufs, 4, 16, AR_FLOAT32, -1), AR_ERR_INVALID_ARG, "AG step -1");
+    rejected(ar_tree_step(ctx, bufs, 8, 16, AR_FLOAT32, AR_SUM, 3), AR_ERR_INVALID_ARG,
+             "tree step 3 of 8 ranks");
+    rejected(ar_dtree_step(ctx, bufs, 8, 16, AR_FLOAT32, AR_SUM, 6), AR_ERR_INVALID_ARG,
+             "dtree step 6 of 8 ranks");
+    rejected(ar_hd_rs_step(ctx, bufs, 6, 16, AR_FLOAT32, AR_SUM, 0), AR_ERR_UNSUPPORTED,
+             "hd step on 6 ranks");
+    rejected(ar_copy(ctx, bufs[0], rank_addr(1, 4), 64), AR_ERR_INVALID_ARG, "copy misaligned");
+    CHECK(fake_counters().kernel_launches == before, "a rejected call launched a kernel");
+
+    CHECK(ar_allreduce(ctx, bufs, 5, 0, AR_FLOAT32, AR_SUM, AR_ALGO_RING_STEP) == AR_OK, "count 0");
+    CHECK(ar_allreduce(ctx, bufs, 1, 99, AR_FLOAT32, AR_AVG, AR_ALGO_TREE) == AR_OK, "one rank");
+    CHECK(fake_counters().kernel_launches == before, "a no-op launched a kernel");
+}
+
+// ------------------------------------------------------- launch sequences
+struct Expect {
+    arlib::Kind kind;
+    int step;
+};
+
+std::vector<Expect> expected(int coll, ar_algo algo, int n) {
+    std::vector<Expect> e;
+    const bool rs = coll != 2, ag = coll != 1;
+    const int L = log2i(n);
+    switch (algo) {
+        case AR_ALGO_RING_FUSED:
+            e.push_back({coll == 0 ? arlib::KIND_FUSED_AR
+                                   : coll == 1 ? arlib::KIND_FUSED_RS : arlib::KIND_FUSED_AG, 0});
+            break;
+        case AR_ALGO_TREE:
+            for (int s = 0; s < L; ++s) e.push_back({arlib::KIND_TREE_STEP, s});
+            break;
+        case AR_ALGO_DOUBLE_TREE:
+            for (int s = 0; s < 2 * L; ++s) e.push_back({arlib::KIND_DT_STEP, s});
+            break;
+        case AR_ALGO_HALVING_DOUBLING:
+            if (rs) for (int s = 0; s < L; ++s) e.push_back({arlib::KIND_HD_RS_STEP, s});
+            if (ag) for (int s = 0; s < L; ++s) e.push_back({arlib::KIND_HD_AG_STEP, s});
+            break;
+        default:
+            if (rs) for (int k = 0; k < n - 1; ++k) e.push_back({arlib::KIND_RS_STEP, k});
+            if (ag) for (int k = 0; k < n - 1; ++k) e.push_back({arlib::KIND_AG_STEP, k});
+            break;
+    }
+    return e;
+}
+
+ar_status call(ar_ctx* ctx, int coll, void** bufs, int n, size_t count, ar_dtype dt, ar_op op,
+               ar_algo algo) {
+    if (coll == 0) return ar_allreduce(ctx, bufs, n, count, dt, op, algo);
+    if (coll == 1) return ar_reduce_scatter(ctx, bufs, n, count, dt, op, algo);
+    return ar_allgather(ctx, bufs, n, count, dt, algo);
+}
+
+void check_sequence(const std::vector<FakeLaunch>& got, int coll, ar_algo algo, int n,
+                    size_t count, ar_dtype dt, ar_op op, void** bufs, const char* what) {
+    const std::vector<Expect> want = expected(coll, algo, n);
+    CHECK(got.size() == want.size(), "%s: %zu launches, want %zu", what, got.size(), want.size());
+    for (size_t i = 0; i < got.size() && i < want.size(); ++i) {
+        const FakeLaunch& l = got[i];
+        CHECK(l.plan.kind == want[i].kind && l.plan.step == want[i].step,
+              "%s: launch %zu is kind %d step %d", what, i, (int)l.plan.kind, l.plan.step);
+        CHECK(l.plan.nranks == n && l.plan.count == count && l.plan.dtype == dt, "%s: plan", what);
+        const bool is_ag = l.plan.kind == arlib::KIND_AG_STEP ||
+                           l.plan.kind == arlib::KIND_HD_AG_STEP ||
+                           l.plan.kind == arlib::KIND_FUSED_AG;
+        if (!is_ag) {   // copy kernels ignore the operator
+            CHECK(l.plan.op == op, "%s: op", what);
+            CHECK(l.args.avg == (op == AR_AVG ? 1 : 0), "%s: avg flag", what);
+        }
+        for (int r = 0; r < n; ++r) CHECK(l.args.t.p[r] == bufs[r], "%s: rank %d pointer", what, r);
+        for (int r = n; r < kMaxN; ++r) CHECK(l.args.t.p[r] == nullptr, "%s: stale pointer", what);
+    }
+}
+
+void check_launches(ar_ctx* ctx) {
+    std::mt19937_64 rng(12345);
+    const ar_algo algos[] = {AR_ALGO_RING_STEP, AR_ALGO_RING_FUSED, AR_ALGO_TREE,
+                             AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE, AR_ALGO_AUTO};
+    const ar_dtype dts[] = {AR_INT32, AR_FLOAT32, AR_BFLOAT16};
+    const ar_op ops[] = {AR_SUM, AR_MAX, AR_AVG};
+    const size_t special[] = {1, 2, 3, 7, 15, 16, 17, 63, 64, 65, 4095, 4096, 4097, 65536,
+                              1000003, size_t(1) << 31, (size_t(1) << 40) + 5};
+    int calls = 0;
+    for (int iter = 0; iter < 4000; ++iter) {
+        const int n = 1 + (int)(rng() % kMaxN);
+        const ar_algo algo = algos[rng() % 6];
+        const int coll = (int)(rng() % 3);
+        const ar_dtype dt = dts[rng() % 3];
+        ar_op op = ops[rng() % 3];
+        if (dt == AR_INT32 && op == AR_AVG) op = AR_SUM;
+        size_t count = rng() % 3 == 0 ? special[rng() % (sizeof special / sizeof special[0])]
+                                      : (size_t)(rng() % 200000);
+        if (rng() % 4 == 0) count = (size_t)n * (count % 5000 + 1);   // N divides count
+        const size_t eb = eb_of(dt);
+        // common alignment shift (vector path) or mixed shifts (element path)
+        const bool mixed = rng() % 5 == 0;
+        const size_t shift = (rng() % (16 / eb)) * eb;
+        void* bufs[kMaxN];
+        for (int r = 0; r < n; ++r)
+            bufs[r] = rank_addr(r, mixed ? ((size_t)r % (16 / eb)) * eb : shift);
+        fake_clear_executed();
+        const ar_status st = call(ctx, coll, bufs, n, count, dt, op, algo);
+        const bool tree_only = algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE;
+        const bool needs_pow2 = tree_only || algo == AR_ALGO_HALVING_DOUBLING;
+        char what[160];
+        std::snprintf(what, sizeof what, "coll %d algo %d n %d count %zu dtype %d op %d shift %zu%s",
+                      coll, (int)algo, n, count, (int)dt, (int)op, shift, mixed ? " mixed" : "");
+        if (tree_only && coll != 0) {
+            CHECK(st == AR_ERR_UNSUPPORTED, "%s: %d", what, (int)st);
+            continue;
+        }
+        if (needs_pow2 && !pow2(n)) {
+            CHECK(st == AR_ERR_UNSUPPORTED, "%s: %d", what, (int)st);
+            continue;
+        }
+        ar_algo resolved = algo;
+        if (algo == AR_ALGO_AUTO) {
+            (void)ar_auto_algo(n, count, dt, &resolved);
+            if ((resolved == AR_ALGO_TREE || resolved == AR_ALGO_DOUBLE_TREE) && coll != 0)
+                resolved = AR_ALGO_RING_FUSED;
+        }
+        // a call whose kernels do not all fit one grid is refused before any launch
+        bool fits = true;
+        if (n > 1)
+            for (const Expect& e : expected(coll, resolved, n)) {
+                arlib::Plan p{};
+                p.kind = e.kind;
+                p.dtype = dt;
+                p.op = op;
+                p.nranks = n;
+                p.count = count;
+                p.step = e.step;
+                p.vec = !mixed;
+                p.mis = mixed ? 0u : (unsigned)shift;
+                arlib::Shape sh;
+                fits = fits && arlib::plan_shape(p, &sh);
+            }
+        if (!fits) {
+            CHECK(st == AR_ERR_INVALID_ARG && fake_executed().empty(),
+                  "%s: oversized call gave %d and %zu launches", what, (int)st,
+                  fake_executed().size());
+            continue;
+        }
+        CHECK(st == AR_OK, "%s: status %d (%s)", what, (int)st, ar_last_error(ctx));
+        if (st != AR_OK) continue;
+        ++calls;
+        if (n == 1) {
+            CHECK(fake_executed().empty(), "%s: one rank launched", what);
+            continue;
+        }
+        check_sequence(fake_executed(), coll, resolved, n, count, dt, op, bufs, what);
+        for (const FakeLaunch& l : fake_executed()) {
+            const bool vec = !mixed;
+            CHECK(l.plan.vec == vec, "%s: vec flag", what);
+            CHECK(l.plan.mis == (vec ? (unsigned)shift : 0u), "%s: mis %u", what, l.plan.mis);
+        }
+    }
+    CHECK(calls > 1000, "too few accepted calls (%d)", calls);
+
+    // single-step entry points launch exactly one kernel of their kind
+    void* bufs[kMaxN];
+    for (int r = 0; r < kMaxN; ++r) bufs[r] = rank_addr(r, 0);
+    for (int n : {2, 3, 8, 64}) {
+        for (int k = 0; k < n - 1; ++k) {
+            fake_clear_executed();
+            CHECK(ar_ring_rs_step(ctx, bufs, n, 1000, AR_FLOAT32, AR_AVG, k) == AR_OK, "rs step");
+            CHECK(ar_ring_ag_step(ctx, bufs, n, 1000, AR_FLOAT32, k) == AR_OK, "ag step");
+            CHECK(fake_executed().size() == 2 && fake_executed()[0].plan.kind == arlib::KIND_RS_STEP &&
+                      fake_executed()[1].plan.kind == arlib::KIND_AG_STEP &&
+                      fake_executed()[0].plan.step == k,
+                  "single ring steps n=%d k=%d", n, k);
+        }
+    }
+}
+
+// ----------------------------------------------------------- graph replay
+bool same_launch(const FakeLaunch& x, const FakeLaunch& y) {
+    const arlib::Args &a = x.args, &b = y.args;
+    for (int r = 0; r < kMaxN; ++r)
+        if (a.t.p[r] != b.t.p[r]) return false;
+    return x.grid == y.grid && x.plan.kind == y.plan.kind && x.plan.step == y.plan.step &&
+           a.count == b.count && a.per == b.per && a.n == b.n && a.step == b.step &&
+           a.tiles == b.tiles && a.mis == b.mis && a.avg == b.avg && a.nf == b.nf &&
+           a.inv == b.inv;
+}
+
+void check_graphs(ar_ctx* ctx) {
+    FakeCounters& fc = fake_counters();
+    void* bufs[kMaxN];
+    for (int r = 0; r < kMaxN; ++r) bufs[r] = rank_addr(r, 0);
+    const ar_algo multi[] = {AR_ALGO_RING_STEP, AR_ALGO_TREE, AR_ALGO_HALVING_DOUBLING,
+                             AR_ALGO_DOUBLE_TREE};
+    for (ar_algo algo : multi) {
+        CHECK(ar_set_graphs(ctx, 0) == AR_OK, "graphs off");
+        fake_clear_executed();
+        CHECK(ar_allreduce(ctx, bufs, 8, 5000, AR_FLOAT32, AR_AVG, algo) == AR_OK, "direct");
+        const std::vector<FakeLaunch> direct = fake_executed();
+        CHECK(ar_set_graphs(ctx, SIZE_MAX) == AR_OK, "graphs on");
+        for (int rep = 0; rep < 3; ++rep) {
+            const long cap = fc.captures, gl = fc.graph_launches;
+            fake_clear_executed();
+            CHECK(ar_allreduce(ctx, bufs, 8, 5000, AR_FLOAT32, AR_AVG, algo) == AR_OK, "replay");
+            CHECK(fc.graph_launches == gl + 1, "algo %d rep %d: no graph launch", (int)algo, rep);
+            CHECK(fc.captures == cap + (rep == 0 ? 1 : 0), "algo %d rep %d: captures", (int)algo, rep);
+            const std::vector<FakeLaunch>& got = fake_executed();
+            CHECK(got.size() == direct.size(), "algo %d: replay launches %zu vs %zu", (int)algo,
+                  got.size(), direct.size());
+            for (size_t i = 0; i < got.size() && i < direct.size(); ++i)
+                CHECK(same_launch(got[i], direct[i]), "algo %d: replayed launch %zu differs",
+                      (int)algo, i);
+        }
+    }
+    // the fused pass is one launch: never replayed
+    {
+        const long gl = fc.graph_launches;
+        CHECK(ar_allreduce(ctx, bufs, 8, 5000, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED) == AR_OK, "fused");
+        CHECK(fc.graph_launches == gl, "fused call went through a graph");
+    }
+    // threshold: 1024 bytes per rank
+    CHECK(ar_set_graphs(ctx, 1024) == AR_OK, "threshold");
+    {
+        const long gl = fc.graph_launches;
+        CHECK(ar_allreduce(ctx, bufs, 4, 256, AR_FLOAT32, AR_SUM, AR_ALGO_RING_STEP) == AR_OK, "small");
+        CHECK(fc.graph_launches == gl + 1, "1024-byte call not replayed");
+        CHECK(ar_allreduce(ctx, bufs, 4, 257, AR_FLOAT32, AR_SUM, AR_ALGO_RING_STEP) == AR_OK, "big");
+        CHECK(fc.graph_launches == gl + 1, "1028-byte call replayed");
+    }
+    // eviction: more distinct shapes than the cache holds
+    CHECK(ar_set_graphs(ctx, SIZE_MAX) == AR_OK, "graphs on");
+    {
+        const long destroyed = fc.execs_destroyed, syncs = fc.event_syncs;
+        for (int i = 0; i < 80; ++i)
+            CHECK(ar_allreduce(ctx, bufs, 4, 100 + (size_t)i, AR_INT32, AR_SUM,
+                               AR_ALGO_RING_STEP) == AR_OK, "eviction call %d", i);
+        CHECK(fc.execs_destroyed > destroyed, "no graph was evicted");
+        CHECK(fc.event_syncs - syncs >= fc.execs_destroyed - destroyed,
+              "an evicted graph was destroyed without waiting for its last replay");
+    }
+    // a caller capturing the context's stream gets direct launches in its capture
+    {
+        std::vector<FakeLaunch> sink;
+        fake_set_null_stream_capturing(true, &sink);
+        const long gl = fc.graph_launches, cap = fc.captures;
+        CHECK(ar_allreduce(ctx, bufs, 8, 777, AR_FLOAT32, AR_SUM, AR_ALGO_DOUBLE_TREE) == AR_OK,
+              "under caller capture");
+        fake_set_null_stream_capturing(false, nullptr);
+        CHECK(fc.graph_launches == gl && fc.captures == cap, "library graph used under capture");
+        CHECK(sink.size() == 6, "caller capture got %zu launches, want 6", sink.size());
+    }
+    CHECK(ar_set_graphs(ctx, 0) == AR_OK, "graphs off");
+    CHECK(fc.execs_created == fc.execs_destroyed, "graphs left after turning replay off");
+    CHECK(fc.events_created == fc.events_destroyed, "events left after turning replay off");
+    CHECK(fc.graphs_created == fc.graphs_destroyed, "captured graphs not destroyed");
+    CHECK(ar_set_graphs(nullptr, 1) == AR_ERR_INVALID_ARG, "NULL ctx");
+}
+
+}  // namespace
+
+int main() {
+    // rank buffers of device 0, and one range on device 1
+    for (int r = 0; r < kMaxN; ++r) fake_register(rank_addr(r, 0), kStride, 0);
+    fake_register(reinterpret_cast<void*>(kBase - kStride), kStride, 1);
+
+    check_chunk_range();
+    check_cost_model();
+
+    ar_ctx* bad = nullptr;
+    CHECK(ar_create(nullptr, 0, nullptr) == AR_ERR_INVALID_ARG, "create NULL out");
+    CHECK(ar_create(&bad, 1, nullptr) == AR_ERR_INVALID_ARG && bad == nullptr, "create device 1");
+    CHECK(std::strlen(ar_last_error(nullptr)) > 0, "create error text");
+    CHECK(ar_destroy(nullptr) == AR_OK, "destroy NULL");
+    for (int s = 0; s <= 5; ++s) CHECK(ar_status_string((ar_status)s) != nullptr, "status string");
+
+    ar_ctx* ctx = nullptr;
+    CHECK(ar_create(&ctx, 0, nullptr) == AR_OK && ctx, "create");
+    if (ctx) {
+        check_validation(ctx);
+        check_launches(ctx);
+        check_graphs(ctx);
+        // leave a few graphs recorded: ar_destroy must release them
+        CHECK(ar_set_graphs(ctx, SIZE_MAX) == AR_OK, "graphs on");
+        void* bufs[kMaxN];
+        for (int r = 0; r < kMaxN; ++r) bufs[r] = rank_addr(r, 0);
+        for (int i = 0; i < 3; ++i)
+            (void)ar_allreduce(ctx, bufs, 4, 10 + (size_t)i, AR_FLOAT32, AR_SUM, AR_ALGO_TREE);
+        CHECK(ar_destroy(ctx) == AR_OK, "destroy");
+    }
+    const FakeCounters& fc = fake_counters();
+    CHECK(fc.execs_created == fc.execs_destroyed && fc.events_created == fc.events_destroyed &&
+              fc.streams_created == fc.streams_destroyed,
+          "ar_destroy left graphs, events or streams behind");
+    const char* msg = nullptr;
+    CHECK(fake_coverage_ok(&msg), "launch coverage: %s", msg);
+    std::printf("launches %ld, graph launches %ld, captures %ld, evictions %ld\n",
+                fc.kernel_launches, fc.graph_launches, fc.captures, fc.execs_destroyed);
+    if (g_fail) {
+        std::printf("%d FAILED\n", g_fail);
+        return 1;
+    }
+    std::printf("ALL OK\n");
+    return 0;
+}

@@ -1,0 +1,106 @@
+"""Poison test: no kernel writes outside the rank buffers it is given.
+
+Every rank buffer is a view into a larger allocation whose leading and
+trailing guard regions hold a sentinel bit pattern; after each collective the
+guards must be bit-for-bit unchanged and the views must hold the oracle's
+result.  Counts cover ragged chunks, counts below N and empty chunks, and the
+views start at several element offsets from a 16-byte boundary, so the
+element-wise head and tail paths run next to the guards."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_allreduce_rs_amd as ar
+from tests.gpu_helpers import assert_bits_equal, to_np
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+GUARD = 67                                     # elements on each side
+SENTINEL = {"int32": np.int32(0x7BADBEEF),
+            "float32": np.uint32(0x7FBADBAD).view(np.float32),
+            "bfloat16": np.uint16(0x7FBB)}
+
+AR_SIMS = {"ring_step": oracle.simulate_ring_allreduce, "ring_fused": oracle.simulate_ring_allreduce,
+           "tree": oracle.simulate_tree_allreduce, "halving_doubling": oracle.simulate_hd_allreduce,
+           "double_tree": oracle.simulate_double_tree_allreduce}
+
+
+def _inputs(dtype, n, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if dtype == "int32":
+        return [rng.integers(-10**6, 10**6, size=count).astype(np.int32) for _ in range(n)]
+    f = [rng.standard_normal(count).astype(np.float32) for _ in range(n)]
+    if dtype == "float32":
+        return f
+    return [torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            for x in f]
+
+
+def _guarded(xs, dtype, shift):
+    """Per rank: an allocation of GUARD + shift + count + GUARD elements filled
+    with the sentinel, with the input copied into the middle; returns the
+    full tensors and the views handed to the library."""
+    fulls, views = [], []
+    for x in xs:
+        host = np.full(GUARD + shift + x.size + GUARD, SENTINEL[dtype])
+        host[GUARD + shift:GUARD + shift + x.size] = x
+        if dtype == "bfloat16":
+            t = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            t = torch.from_numpy(host).cuda()
+        fulls.append(t)
+        views.append(t[GUARD + shift:GUARD + shift + x.size])
+    return fulls, views
+
+
+def _check_guards(fulls, dtype, shift, count, what):
+    for r, t in enumerate(fulls):
+        h = to_np(t)
+        assert_bits_equal(h[:GUARD + shift], np.full(GUARD + shift, SENTINEL[dtype]),
+                          f"{what}: leading guard of rank {r}")
+        assert_bits_equal(h[GUARD + shift + count:], np.full(GUARD, SENTINEL[dtype]),
+                          f"{what}: trailing guard of rank {r}")
+
+
+CASES = [(8, 1), (8, 7), (8, 1001), (3, 10007), (16, 4099), (64, 130), (64, 70_001)]
+
+
+@pytest.mark.parametrize("algo", sorted(AR_SIMS))
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "max")])
+@pytest.mark.parametrize("n,count", CASES)
+def test_allreduce_writes_only_its_buffers(algo, dtype, op, n, count):
+    if algo in ("tree", "halving_doubling", "double_tree") and n & (n - 1):
+        pytest.skip("needs a power-of-two rank count")
+    xs = _inputs(dtype, n, count, seed=n * 613 + count)
+    want = AR_SIMS[algo](xs, dtype, op).state
+    for shift in (0, 1, 3):
+        fulls, views = _guarded(xs, dtype, shift)
+        ar.allreduce(views, op=op, algo=algo)
+        torch.cuda.synchronize()
+        what = f"{algo} {dtype} {op} n={n} count={count} shift={shift}"
+        _check_guards(fulls, dtype, shift, count, what)
+        for r in range(n):
+            assert_bits_equal(to_np(views[r]), want[r], f"{what} rank {r}")
+
+
+@pytest.mark.parametrize("algo", ["ring_step", "ring_fused", "halving_doubling"])
+@pytest.mark.parametrize("n,count", CASES)
+def test_reduce_scatter_and_allgather_write_only_their_buffers(algo, n, count):
+    if algo == "halving_doubling" and n & (n - 1):
+        pytest.skip("needs a power-of-two rank count")
+    dtype, op = "float32", "sum"
+    xs = _inputs(dtype, n, count, seed=n * 919 + count)
+    for shift in (0, 2):
+        fulls, views = _guarded(xs, dtype, shift)
+        ar.reduce_scatter(views, op=op, algo=algo)
+        torch.cuda.synchronize()
+        _check_guards(fulls, dtype, shift, count, f"RS {algo} n={n} count={count} shift={shift}")
+        ar.allgather(views, algo=algo)
+        torch.cuda.synchronize()
+        _check_guards(fulls, dtype, shift, count, f"AG {algo} n={n} count={count} shift={shift}")
+        want = AR_SIMS[algo](xs, dtype, op).state
+        for r in range(n):
+            assert_bits_equal(to_np(views[r]), want[r], f"RS+AG {algo} n={n} rank {r}")
