@@ -43,7 +43,8 @@ ALWAYS_REPLAY = 1 << 62         # graph-replay threshold that covers every size 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # the sources the fused kernel and the calibration copy are built from
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_rs_amd", "csrc", f)
-                  for f in ("common.h", "elem.h", "fused.hip", "copy.hip")]
+                  for f in ("common.h", "elem.h", "launch.h", "fused_impl.h", "fused.hip",
+                            "fused_f32.hip", "copy.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -77,7 +78,7 @@ def parse():
     ap.add_argument("--workload", default=W.DDP_BUCKET.name, choices=sorted(names))
     ap.add_argument("--algo", default="ring_fused",
                     choices=["ring_fused", "ring_step", "tree", "halving_doubling",
-                             "double_tree"])
+                             "double_tree", "tree_fused", "halving_doubling_fused"])
     ap.add_argument("--sets", type=int, default=0,
                     help="bucket sets to rotate over (0: enough to exceed the Infinity Cache 4x)")
     ap.add_argument("--seed", type=int, default=0)
@@ -143,15 +144,27 @@ def copy_ceiling(ar, nbytes, reps=50):
     return 2 * nb / (ms * 1e-3) / 1e9, ms
 
 
-def cpu_baseline(w, sets_host, gpu_first, min_seconds):
+def oracle_allreduce(algo):
+    """The oracle's message-passing simulation of `algo` (test infrastructure)."""
+    import oracle
+    if algo in ("tree", "tree_fused"):
+        return oracle.simulate_tree_allreduce
+    if algo in ("halving_doubling", "halving_doubling_fused"):
+        return oracle.simulate_hd_allreduce
+    if algo == "double_tree":
+        return oracle.simulate_double_tree_allreduce
+    return oracle.simulate_ring_allreduce
+
+
+def cpu_baseline(w, algo, sets_host, gpu_first, min_seconds):
     """Time the CPU oracle on the workload; also check the GPU's first result."""
     import numpy as np
-    import oracle
+    sim = oracle_allreduce(algo)
     reps, t_total = 0, 0.0
     out = None
     while t_total < min_seconds or reps == 0:
         t0 = time.perf_counter()
-        out = oracle.simulate_ring_allreduce(sets_host, w.dtype, w.op).state
+        out = sim(sets_host, w.dtype, w.op).state
         t_total += time.perf_counter() - t0
         reps += 1
     ok = all(np.array_equal(np.ascontiguousarray(g).view(np.uint8),
@@ -165,7 +178,7 @@ def cpu_baseline(w, sets_host, gpu_first, min_seconds):
         "cores": 1,
         "kind": "oracle",
         "sample": (f"whole workload ({w.nranks} ranks x {w.count} {w.dtype}, {w.op}) through "
-                   f"oracle.simulate_ring_allreduce, {reps} run(s), {per:.3f} s each; numpy "
+                   f"oracle.{sim.__name__}, {reps} run(s), {per:.3f} s each; numpy "
                    "elementwise kernels, single thread"),
         "seconds_per_allreduce": round(per, 4),
     }, ok
@@ -178,8 +191,8 @@ METRIC = "AllReduce GB/s + % of HBM peak, N=8 ranks \u00d7 25 MB fp32, 1 MI355X"
 def step_bytes(w, algo):
     """HBM bytes one AllReduce moves with each algorithm (K = bytes per rank)."""
     n, k = w.nranks, w.bytes_per_rank
-    if algo == "ring_fused":
-        return 2 * n * k                      # N*K read + N*K written
+    if algo.endswith("_fused"):
+        return 2 * n * k                      # one pass: N*K read + N*K written
     if algo in ("ring_step", "halving_doubling"):
         return 5 * (n - 1) * k                # ReduceScatter 3(N-1)K + AllGather 2(N-1)K
     if algo == "double_tree":
@@ -196,11 +209,12 @@ def sweep(args):
 
     import ring_allreduce_rs_amd as ar
     import workloads as W
-    base = ("ring_step", "tree", "halving_doubling", "double_tree", "ring_fused")
+    base = ("ring_step", "tree", "halving_doubling", "double_tree", "ring_fused", "tree_fused",
+            "halving_doubling_fused")
     # "+graph": the same algorithm replayed from a library-recorded HIP graph
     algos = base + tuple(a + "+graph" for a in base[:4])
     launches = {"ring_step": 2 * 63, "tree": 6, "halving_doubling": 12, "double_tree": 12,
-                "ring_fused": 1}
+                "ring_fused": 1, "tree_fused": 1, "halving_doubling_fused": 1}
     launches.update({a + "+graph": launches[a] for a in base[:4]})
     rows = {a: [] for a in algos}
     for w in W.SWEEP:
@@ -336,7 +350,8 @@ def main():
             "kernel": {"ring_fused": "k_fused", "ring_step": "k_rs_step/k_ag_step",
                        "tree": "k_tree_step",
                        "halving_doubling": "k_hd_rs_step/k_hd_ag_step",
-                       "double_tree": "k_dtree_step"}[args.algo],
+                       "double_tree": "k_dtree_step", "tree_fused": "k_fused",
+                       "halving_doubling_fused": "k_fused"}[args.algo],
             "us_per_launch": round(ms * 1e3, 3),
             "algorithmic_bytes_per_launch": alg_bytes,
         },
@@ -344,12 +359,13 @@ def main():
     }
     if not args.no_others:
         others = {}
-        for algo in ("ring_fused", "ring_step", "tree", "halving_doubling", "double_tree"):
-            if algo == args.algo or (algo in ("tree", "halving_doubling", "double_tree")
+        for algo in ("ring_fused", "ring_step", "tree", "halving_doubling", "double_tree",
+                     "tree_fused", "halving_doubling_fused"):
+            if algo == args.algo or (algo not in ("ring_fused", "ring_step")
                                      and w.nranks & (w.nranks - 1)):
                 continue
             reps = max(5, min(args.steps // 4, 100))
-            for graph in ((False, True) if algo != "ring_fused" else (False,)):
+            for graph in ((False, True) if not algo.endswith("_fused") else (False,)):
                 ar.set_graphs(graph, max_bytes_per_rank=ALWAYS_REPLAY)
                 wl, m = time_algo(ar, sets, w, algo, reps, 3)
                 ar.set_graphs(False)
@@ -378,7 +394,7 @@ def main():
                                   "us": round(cms * 1e3, 2)}
         out["others"] = others
     if not args.no_cpu_baseline and host is not None:
-        cb, ok = cpu_baseline(w, host, gpu_first, args.cpu_seconds)
+        cb, ok = cpu_baseline(w, args.algo, host, gpu_first, args.cpu_seconds)
         cb["host_cpus"] = os.cpu_count()
         out["cpu_baseline"] = cb
         out["parity_vs_oracle"] = "bitwise" if ok else "MISMATCH"

@@ -59,8 +59,9 @@ typedef struct ar_ctx ar_ctx;
 typedef enum ar_status AR_ENUM_INT {
     AR_OK = 0,
     AR_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum, overlap, step index */
-    AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, TREE / HALVING_DOUBLING /
-                                 DOUBLE_TREE on non-power-of-two N, TREE / DOUBLE_TREE on
+    AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, the tree algorithms
+                                 (TREE, HALVING_DOUBLING, DOUBLE_TREE and their fused forms)
+                                 on non-power-of-two N, TREE / TREE_FUSED / DOUBLE_TREE on
                                  ReduceScatter / AllGather */
     AR_ERR_RUNTIME = 3,       /* the HIP runtime reported an error */
     AR_ERR_NO_MEMORY = 4      /* host allocation of the context failed */
@@ -108,6 +109,16 @@ typedef enum ar_op AR_ENUM_INT { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
  *                v and carries the rest.  A node folds (left + own) + right;
  *                the root folds own + child.  2 log2 N steps; power-of-two N;
  *                AllReduce only.
+ *  TREE_FUSED -- the TREE result (same bits) in one pass: every element is read
+ *                once from each rank, folded as the pairwise tree of recursive
+ *                doubling in registers, and written to all N ranks (the
+ *                minimum N*K read + N*K written, like RING_FUSED).
+ *                Power-of-two N; AllReduce only.
+ *  HALVING_DOUBLING_FUSED -- the HALVING_DOUBLING result (same bits) in one
+ *                pass: the pairwise tree over ranks in bit-reversed order
+ *                (partners at distance N/2 first).  Power-of-two N;
+ *                AllReduce, ReduceScatter (owner chunk written) and AllGather
+ *                (a copy, as for every algorithm).
  *  AUTO       -- pick the algorithm with the smallest predicted time under the
  *                latency/bandwidth model of ar_predict_us (the pages' size-based
  *                choice between ring and tree: "AllReduce", compassingai.com,
@@ -120,7 +131,9 @@ typedef enum ar_algo AR_ENUM_INT {
     AR_ALGO_TREE = 2,
     AR_ALGO_HALVING_DOUBLING = 3,
     AR_ALGO_AUTO = 4,
-    AR_ALGO_DOUBLE_TREE = 5
+    AR_ALGO_DOUBLE_TREE = 5,
+    AR_ALGO_TREE_FUSED = 6,
+    AR_ALGO_HALVING_DOUBLING_FUSED = 7
 } ar_algo;
 
 /* Create a context bound to HIP device `device` and stream `stream`

@@ -11,6 +11,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,14 +20,16 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libar.so")
 
-SOURCES = ["fused.hip", "steps.hip", "copy.hip", "dispatch.hip", "ar_api.cpp"]
+# the fused kernels are instantiated per element type so the (slowest) device
+# compilations run side by side
+SOURCES = ["fused_f32.hip", "fused_bf16.hip", "fused_i32.hip", "fused.hip", "steps.hip",
+           "copy.hip", "dispatch.hip", "ar_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-fvisibility=hidden",
     # exact per-hop arithmetic: no contraction, IEEE division, subnormals kept
     "-ffp-contract=off",
@@ -44,19 +48,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libar.so)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source into ring_allreduce_rs_amd/libar.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd[-3:])}")
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source (in parallel) and link ring_allreduce_rs_amd/libar.so;
+    returns its path."""
+    flags = [*FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC]
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1)), 16))
+    with tempfile.TemporaryDirectory(prefix="ar_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+        cmds = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([hipcc(), *FLAGS, *(extra_flags or []), "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -25,7 +25,7 @@ AR_ERR_NO_MEMORY = 4
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {"sum": 0, "max": 1, "avg": 2}
 ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2, "halving_doubling": 3, "auto": 4,
-         "double_tree": 5}
+         "double_tree": 5, "tree_fused": 6, "halving_doubling_fused": 7}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 # every symbol include/ar.h declares

@@ -89,9 +89,15 @@ size_t elem_bytes(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
 
 bool valid_dtype(int d) { return d == AR_INT32 || d == AR_FLOAT32 || d == AR_BFLOAT16; }
 bool valid_op(int o) { return o == AR_SUM || o == AR_MAX || o == AR_AVG; }
-bool valid_algo(int a) {
-    return a == AR_ALGO_RING_STEP || a == AR_ALGO_RING_FUSED || a == AR_ALGO_TREE ||
-           a == AR_ALGO_HALVING_DOUBLING || a == AR_ALGO_AUTO || a == AR_ALGO_DOUBLE_TREE;
+bool valid_algo(int a) { return a >= AR_ALGO_RING_STEP && a <= AR_ALGO_HALVING_DOUBLING_FUSED; }
+// algorithms defined for power-of-two rank counts only
+bool needs_pow2(int a) {
+    return a == AR_ALGO_TREE || a == AR_ALGO_HALVING_DOUBLING || a == AR_ALGO_DOUBLE_TREE ||
+           a == AR_ALGO_TREE_FUSED || a == AR_ALGO_HALVING_DOUBLING_FUSED;
+}
+// algorithms that exist as AllReduce only
+bool allreduce_only(int a) {
+    return a == AR_ALGO_TREE || a == AR_ALGO_DOUBLE_TREE || a == AR_ALGO_TREE_FUSED;
 }
 int log2_exact(int n) {
     int l = 0;
@@ -148,6 +154,8 @@ double predict_allreduce_us(int algo, int n, size_t count, size_t eb) {
     if (n == 1 || count == 0) return kCallUs;
     switch (algo) {
         case AR_ALGO_RING_FUSED:
+        case AR_ALGO_TREE_FUSED:
+        case AR_ALGO_HALVING_DOUBLING_FUSED:
             return kCallUs + 2.0 * n * k / (fused_gbps(n) * 1e3);
         case AR_ALGO_RING_STEP:
             return kCallUs + (2.0 * (n - 1) - 1) * kLaunchUs + 5.0 * (n - 1) * k / (kStepGBps * 1e3);
@@ -299,7 +307,7 @@ arlib::RankTable table_of(void* const* bufs, int nranks) {
 }
 
 arlib::Plan make_plan(arlib::Kind k, int dtype, int op, int nranks, size_t count, int step,
-                      bool vec, unsigned mis) {
+                      bool vec, unsigned mis, int order = arlib::ORDER_RING) {
     arlib::Plan p;
     p.kind = k;
     p.dtype = (ar_dtype)dtype;
@@ -309,6 +317,7 @@ arlib::Plan make_plan(arlib::Kind k, int dtype, int op, int nranks, size_t count
     p.step = step;
     p.vec = vec;
     p.mis = mis;
+    p.order = order;
     return p;
 }
 
@@ -338,16 +347,24 @@ struct Launch {
 // The kernels of L, in launch order.
 std::vector<arlib::Plan> plans_of(const Launch& L) {
     std::vector<arlib::Plan> ps;
-    auto add = [&](arlib::Kind k, int st) {
-        ps.push_back(make_plan(k, L.dtype, L.op, L.nranks, L.count, st, L.vec, L.mis));
+    auto add = [&](arlib::Kind k, int st, int order = arlib::ORDER_RING) {
+        ps.push_back(make_plan(k, L.dtype, L.op, L.nranks, L.count, st, L.vec, L.mis, order));
     };
+    const arlib::Kind fused = L.coll == COLL_AR   ? arlib::KIND_FUSED_AR
+                              : L.coll == COLL_RS ? arlib::KIND_FUSED_RS
+                                                  : arlib::KIND_FUSED_AG;
     const int levels = log2_exact(L.nranks);
     const bool rs = L.coll != COLL_AG, ag = L.coll != COLL_RS;
     switch (L.algo) {
         case AR_ALGO_RING_FUSED:
-            add(L.coll == COLL_AR   ? arlib::KIND_FUSED_AR
-                : L.coll == COLL_RS ? arlib::KIND_FUSED_RS
-                                    : arlib::KIND_FUSED_AG, 0);
+            add(fused, 0);
+            break;
+        case AR_ALGO_TREE_FUSED:
+            add(fused, 0, arlib::ORDER_PAIR);
+            break;
+        case AR_ALGO_HALVING_DOUBLING_FUSED:
+            // the AllGather half is a copy, whatever the order
+            add(fused, 0, L.coll == COLL_AG ? arlib::ORDER_RING : arlib::ORDER_PAIR_BITREV);
             break;
         case AR_ALGO_HALVING_DOUBLING:
             if (rs) for (int st = 0; st < levels; ++st) add(arlib::KIND_HD_RS_STEP, st);
@@ -527,16 +544,14 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
         if (algo == AR_ALGO_AUTO) {
             // ReduceScatter / AllGather alone follow the AllReduce choice, minus TREE
             algo = auto_algo(nranks, count, elem_bytes((ar_dtype)dtype));
-            if ((algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE) && coll != COLL_AR)
-                algo = AR_ALGO_RING_FUSED;
+            if (allreduce_only(algo) && coll != COLL_AR) algo = AR_ALGO_RING_FUSED;
             if (debug_enabled()) std::fprintf(stderr, "[ar] AUTO -> algo %d\n", algo);
         }
-        if ((algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE) && coll != COLL_AR)
+        if (allreduce_only(algo) && coll != COLL_AR)
             return fail(ctx, AR_ERR_UNSUPPORTED,
-                        "TREE and DOUBLE_TREE are AllReduce algorithms; use RING_STEP, "
-                        "RING_FUSED or HALVING_DOUBLING");
-        if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING ||
-             algo == AR_ALGO_DOUBLE_TREE) && !pow2(nranks))
+                        "TREE, TREE_FUSED and DOUBLE_TREE are AllReduce algorithms; use "
+                        "RING_STEP, RING_FUSED, HALVING_DOUBLING or HALVING_DOUBLING_FUSED");
+        if (needs_pow2(algo) && !pow2(nranks))
             return fail(ctx, AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two nranks, got %d",
                         algo, nranks);
         if (count == 0 || nranks == 1) return AR_OK;
@@ -683,9 +698,7 @@ ar_status ar_predict_us(ar_algo algo, int nranks, size_t count, ar_dtype dtype, 
     if (!us || nranks < 1 || nranks > AR_MAX_RANKS || !valid_dtype((int)dtype) ||
         !valid_algo((int)algo) || algo == AR_ALGO_AUTO)
         return AR_ERR_INVALID_ARG;
-    if ((algo == AR_ALGO_TREE || algo == AR_ALGO_HALVING_DOUBLING ||
-         algo == AR_ALGO_DOUBLE_TREE) && !pow2(nranks))
-        return AR_ERR_UNSUPPORTED;
+    if (needs_pow2((int)algo) && !pow2(nranks)) return AR_ERR_UNSUPPORTED;
     *us = predict_allreduce_us((int)algo, nranks, count, elem_bytes(dtype));
     return AR_OK;
 }

@@ -68,6 +68,7 @@ struct FusedTiny {
     static constexpr bool kWrapLoads = true;
 };
 enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_MID = 2, CFG_TINY = 3 };
+#define CFG_MID_VALUE 2   // for the preprocessor: MID kernels exist only when forced
 constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
 // Streaming (non-temporal) loads and stores.  The fused kernel touches every
 // byte once, so caching it only evicts useful lines: on MI355X 8 x 25 MiB went
@@ -173,6 +174,9 @@ int fused_units_per_lane(int cfg);
 
 // Launchers, one per translation unit.
 hipError_t launch_fused_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+hipError_t launch_fused_i32(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+hipError_t launch_fused_f32(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+hipError_t launch_fused_bf16(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
 hipError_t launch_step_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
 
 }  // namespace arlib

@@ -20,6 +20,9 @@ int fused_variant(const Plan& p) {
     const size_t per = ceil_div(p.count, (size_t)p.nranks) * (size_t)elem_bytes(p.dtype);
     if (p.nranks > FusedDeep::B && per <= (size_t)AR_FUSED_TINY_MAX_CHUNK_BYTES) return CFG_TINY;
     if (p.dtype == AR_BFLOAT16 || p.nranks > 16) return CFG_DEEP;
+    // the pairwise orders have a WIDE kernel for 8 ranks only (a wider one
+    // would need a deeper stack of subtree results in registers)
+    if (p.order != ORDER_RING) return AR_SPECIALIZE_N && p.nranks == 8 && p.vec ? CFG_WIDE : CFG_DEEP;
     if (p.nranks <= kBatch) return CFG_WIDE;
     return per <= (size_t)AR_FUSED_DEEP_MAX_CHUNK_BYTES ? CFG_DEEP : CFG_WIDE;
 }

@@ -1,0 +1,259 @@
+// fused_impl.h -- the one-pass ring AllReduce / ReduceScatter / AllGather kernel
+// (templates; instantiated per element type by fused_<type>.hip).
+//
+// Ring schedule (pwwt.cn page "Allreduce：大模型分布式训练的核心通信算法与优化实践",
+// section 2.2, read as: ReduceScatter step k sends chunk (r-k-1) mod N from
+// rank r to rank r+1; AllGather step k forwards chunk (r-k) mod N).  Chunk c
+// is therefore folded over ranks c+1, c+2, ..., c-1, c, left to right, and
+// ends on rank c.  k_fused reads each 16-byte unit of chunk c from every rank
+// (in that order, kBatch ranks of loads in flight before the adds), folds in
+// registers with the same per-hop rounding as the per-step ring, and stores
+// the result to all N ranks (AllReduce), to the owner only (ReduceScatter), or
+// copies the owner's unit to the others (AllGather): 2*N*K bytes for an
+// AllReduce, the minimum.
+//
+// Block -> work mapping: block b handles tile (b mod tiles) of chunk
+// (b / tiles), so the chunk -- and with it the first rank of the fold and
+// every rank pointer -- is uniform across the block and lives in scalar
+// registers.  A chunk whose start is not 16-byte aligned (counts not divisible
+// by N, e.g. 268,435,459 over 16 ranks) has a head of up to 15 bytes and a
+// tail, handled element by element by lanes of the chunk's first tile.
+#pragma once
+
+#include "common.h"
+
+namespace arlib {
+
+// Units ubase, ubase+kFusedThreads, ... (CFG::U of them, bounded by `units`)
+// of the range starting at byte offset byte0 in every rank buffer; CFG::B
+// ranks of loads are issued before they are folded.  NR > 0 fixes the rank
+// count at compile time (loops fully unrolled); NR == 0 reads it from the
+// arguments.
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+template <class Op, int MODE, bool VEC, int NR, class CFG, int ORDER = ORDER_RING>
+__device__ __forceinline__ void fused_units(const Args& a, int c, int start, size_t byte0,
+                                            size_t ubase, size_t units) {
+    using X = Unit<Op, VEC, kFusedNT>;
+    using T = typename X::T;
+    constexpr int U = CFG::U;
+    constexpr int kB = CFG::B;
+    const int n = NR > 0 ? NR : a.n;
+    bool ok[U];
+    size_t off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t idx = ubase + (size_t)u * kFusedThreads;
+        ok[u] = idx < units;
+        off[u] = byte0 + idx * X::kBytes;
+    }
+    T acc[U];
+    if constexpr (MODE == KIND_FUSED_AG) {
+        const char* src = rank_ptr(a, c);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+        for (int r = 0; r < n; ++r) {
+            if (r == c) continue;
+            char* dst = rank_ptr(a, r);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) X::st(dst + off[u], acc[u]);
+        }
+        return;
+    } else if constexpr (ORDER != ORDER_RING) {
+        // Pairwise tree over positions 0..n-1 (n a power of two); position q
+        // holds rank q (PAIR) or rank bitrev(q) (PAIR_BITREV).  Each batch of
+        // bn positions is folded as a subtree; batch results are merged as
+        // they arrive, batch k taking its left partners from the levels whose
+        // bit is set in k (a binary counter), which is the same balanced tree.
+        // Every operator here is commutative, so a node's operand order does
+        // not change its bits.
+        (void)start;
+        const int lg = 31 - __builtin_clz((unsigned)n);
+        const int bn = n < kB ? n : kB;
+        constexpr int kLevels = ilog2((NR > 0 ? NR : AR_MAX_RANKS) / kB);
+        T st[kLevels > 0 ? kLevels : 1][U];
+#pragma unroll
+        for (int j0 = 0; j0 < (NR > 0 ? NR : AR_MAX_RANKS); j0 += kB) {
+            if (NR == 0 && j0 >= n) break;
+            const int k = j0 / kB;
+            T v[kB][U];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                if (CFG::kWrapLoads || j < bn) {
+                    const int q = j0 + (j & (bn - 1));
+                    const int rank = ORDER == ORDER_PAIR || lg == 0
+                                         ? q
+                                         : (int)(__builtin_bitreverse32((unsigned)q) >> (32 - lg));
+                    const char* src = rank_ptr(a, rank);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[j][u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+                }
+            }
+            if constexpr (CFG::kWrapLoads) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int w = 1; w < kB; w *= 2) {
+#pragma unroll
+                for (int j = 0; j + w < kB; j += 2 * w) {
+                    if (j + w < bn) {
+#pragma unroll
+                        for (int u = 0; u < U; ++u) v[j][u] = X::comb(v[j][u], v[j + w][u]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] = v[0][u];
+#pragma unroll
+            for (int l = 0; l < kLevels; ++l) {
+                if ((k >> l) & 1) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[u] = X::comb(st[l][u], acc[u]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) st[l][u] = acc[u];
+                    break;
+                }
+            }
+        }
+    }
+    if constexpr (MODE != KIND_FUSED_AG) {
+        if constexpr (ORDER == ORDER_RING) {
+        // ring order: start = c+1, then c+2, ..., ending with c itself
+        int r = start;
+#pragma unroll
+        for (int j0 = 0; j0 < (NR > 0 ? NR : AR_MAX_RANKS); j0 += kB) {
+            if (NR == 0 && j0 >= n) break;
+            T v[kB][U];
+            int rr = r;
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                // kWrapLoads: issue every slot's load (ranks wrap mod n, so the
+                // addresses stay valid) and keep only the first n in the fold;
+                // a uniform guard here lets the compiler serialise the loads
+                if (CFG::kWrapLoads || j0 + j < n) {
+                    const char* src = rank_ptr(a, rr);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[j][u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+                    rr = (rr + 1 == n) ? 0 : rr + 1;
+                }
+            }
+            // keep the adds behind the whole batch: one memory round trip
+            if constexpr (CFG::kWrapLoads) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                if (j0 + j < n) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        acc[u] = (j0 + j == 0) ? v[j][u] : X::comb(acc[u], v[j][u]);
+                }
+            }
+            r = rr;
+        }
+        }  // ORDER_RING
+        if (a.avg) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] = X::fin(acc[u], a.nf, a.inv);
+        }
+        if constexpr (MODE == KIND_FUSED_RS) {
+            char* dst = rank_ptr(a, c);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) X::st(dst + off[u], acc[u]);
+        } else {
+#pragma unroll
+            for (int r2 = 0; r2 < (NR > 0 ? NR : AR_MAX_RANKS); ++r2) {
+                if (NR == 0 && r2 >= n) break;
+                char* dst = rank_ptr(a, r2);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (ok[u]) X::st(dst + off[u], acc[u]);
+            }
+        }
+    }
+}
+
+template <class Op, int MODE, bool VEC, int NR, class CFG, int ORDER = ORDER_RING>
+__global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
+    constexpr int EB = Op::kElemBytes;
+    const int n = NR > 0 ? NR : a.n;
+    const int c = (int)(blockIdx.x / a.tiles);
+    const unsigned tile = blockIdx.x - (unsigned)c * a.tiles;
+    size_t lo, len;
+    chunk_bounds(a, c, lo, len);
+    if (len == 0) return;
+    const Span sp = make_span<EB, VEC>(lo, len, a.mis);
+    const int start = (c + 1 == n) ? 0 : c + 1;
+    const size_t ubase = (size_t)tile * (kFusedThreads * CFG::U) + threadIdx.x;
+    if (ubase < sp.units)
+        fused_units<Op, MODE, VEC, NR, CFG, ORDER>(a, c, start, sp.body * EB, ubase, sp.units);
+    if constexpr (VEC) {
+        // heads have at most 15 bytes (< 8 elements), as do tails
+        if (tile == 0) {
+            const unsigned t = threadIdx.x;
+            if (t < sp.nhead)
+                fused_units<Op, MODE, false, NR, FusedDeep, ORDER>(a, c, start, (lo + t) * EB, 0,
+                                                                   1);
+            else if (t >= kTailLane && t - kTailLane < sp.ntail)
+                fused_units<Op, MODE, false, NR, FusedDeep, ORDER>(a, c, start,
+                                                            (sp.tail + (t - kTailLane)) * EB, 0, 1);
+        }
+    }
+}
+
+template <class Op, int MODE, bool VEC, int ORDER>
+inline hipError_t launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    const dim3 block(kFusedThreads);
+    const int cfg = fused_variant(p);
+    const bool n8 = AR_SPECIALIZE_N && VEC && p.nranks == 8;
+    if (cfg == CFG_TINY) {
+        // element-wise units whatever the alignment (the grid was sized so)
+        hipLaunchKernelGGL((k_fused<Op, MODE, false, 0, FusedTiny, ORDER>), grid, block, 0, s, a);
+    } else if (cfg == CFG_DEEP) {
+        // the runtime-N loop measured faster than the 8-rank unrolled one here
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep, ORDER>), grid, block, 0, s, a);
+#if AR_FUSED_FORCE_CFG == CFG_MID_VALUE
+    } else if (cfg == CFG_MID) {
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedMid, ORDER>), grid, block, 0, s, a);
+#endif
+    } else if (n8) {
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide, ORDER>), grid, block, 0, s, a);
+    } else if constexpr (ORDER == ORDER_RING) {
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedWide>), grid, block, 0, s, a);
+    } else {
+        return hipErrorInvalidConfiguration;   // no such kernel (fused_variant never asks)
+    }
+    return hipSuccess;
+}
+
+template <class Op, int MODE, int ORDER>
+inline hipError_t launch_fused_v(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    return p.vec ? launch_fused_n<Op, MODE, true, ORDER>(p, a, grid, s)
+                 : launch_fused_n<Op, MODE, false, ORDER>(p, a, grid, s);
+}
+
+template <class Op>
+inline hipError_t launch_fused_op(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    const bool rs = p.kind == KIND_FUSED_RS;
+    if (p.kind != KIND_FUSED_AR && !rs) return hipErrorInvalidValue;
+    hipError_t e = hipErrorInvalidValue;
+    switch (p.order) {
+        case ORDER_RING:
+            e = rs ? launch_fused_v<Op, KIND_FUSED_RS, ORDER_RING>(p, a, grid, s)
+                   : launch_fused_v<Op, KIND_FUSED_AR, ORDER_RING>(p, a, grid, s);
+            break;
+        case ORDER_PAIR:   // recursive doubling: AllReduce only
+            if (!rs) e = launch_fused_v<Op, KIND_FUSED_AR, ORDER_PAIR>(p, a, grid, s);
+            break;
+        case ORDER_PAIR_BITREV:
+            e = rs ? launch_fused_v<Op, KIND_FUSED_RS, ORDER_PAIR_BITREV>(p, a, grid, s)
+                   : launch_fused_v<Op, KIND_FUSED_AR, ORDER_PAIR_BITREV>(p, a, grid, s);
+            break;
+        default:
+            break;
+    }
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
+}  // namespace arlib

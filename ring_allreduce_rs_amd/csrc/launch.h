@@ -28,6 +28,14 @@ enum Kind {
     KIND_DT_STEP = 8,    // one double-binary-tree step (reduce up / broadcast down)
 };
 
+// Fold order of the one-pass kernels.  RING: chunk c is folded over ranks
+// c+1, ..., c (the ring's order).  PAIR: a pairwise tree over ranks 0..N-1 in
+// index order (recursive doubling's result).  PAIR_BITREV: the same tree over
+// ranks in bit-reversed order, i.e. partners at distance N/2 first
+// (recursive halving-doubling's result).  The pairwise orders need a
+// power-of-two N.
+enum Order { ORDER_RING = 0, ORDER_PAIR = 1, ORDER_PAIR_BITREV = 2 };
+
 struct Plan {
     Kind kind;
     ar_dtype dtype;
@@ -37,6 +45,7 @@ struct Plan {
     int step;           // step index for the *_STEP kinds
     bool vec;           // 16-byte path (all buffers share their address mod 16)
     unsigned mis;       // that common address mod 16, in bytes
+    int order = ORDER_RING;   // fold order of the fused kinds (Order)
 };
 
 // Grid / block shape a plan launches with (for logging and tests).

@@ -73,7 +73,8 @@ void check_chunk_range() {
 // ------------------------------------------------------------- cost model
 void check_cost_model() {
     const ar_algo algos[] = {AR_ALGO_RING_STEP, AR_ALGO_RING_FUSED, AR_ALGO_TREE,
-                             AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE};
+                             AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE, AR_ALGO_TREE_FUSED,
+                             AR_ALGO_HALVING_DOUBLING_FUSED};
     const ar_dtype dts[] = {AR_INT32, AR_FLOAT32, AR_BFLOAT16};
     for (int n = 1; n <= kMaxN; ++n)
         for (ar_dtype dt : dts)
@@ -85,7 +86,8 @@ void check_cost_model() {
                     double us = -1;
                     const ar_status st = ar_predict_us(a, n, count, dt, &us);
                     const bool needs_pow2 = a == AR_ALGO_TREE || a == AR_ALGO_HALVING_DOUBLING ||
-                                            a == AR_ALGO_DOUBLE_TREE;
+                                            a == AR_ALGO_DOUBLE_TREE || a == AR_ALGO_TREE_FUSED ||
+                                            a == AR_ALGO_HALVING_DOUBLING_FUSED;
                     if (needs_pow2 && !pow2(n)) {
                         CHECK(st == AR_ERR_UNSUPPORTED, "predict needs pow2");
                         continue;
@@ -186,12 +188,20 @@ struct Expect {
     int step;
 };
 
+int order_of(int coll, ar_algo algo) {
+    if (algo == AR_ALGO_TREE_FUSED) return arlib::ORDER_PAIR;
+    if (algo == AR_ALGO_HALVING_DOUBLING_FUSED && coll != 2) return arlib::ORDER_PAIR_BITREV;
+    return arlib::ORDER_RING;
+}
+
 std::vector<Expect> expected(int coll, ar_algo algo, int n) {
     std::vector<Expect> e;
     const bool rs = coll != 2, ag = coll != 1;
     const int L = log2i(n);
     switch (algo) {
         case AR_ALGO_RING_FUSED:
+        case AR_ALGO_TREE_FUSED:
+        case AR_ALGO_HALVING_DOUBLING_FUSED:
             e.push_back({coll == 0 ? arlib::KIND_FUSED_AR
                                    : coll == 1 ? arlib::KIND_FUSED_RS : arlib::KIND_FUSED_AG, 0});
             break;
@@ -244,7 +254,8 @@ void check_sequence(const std::vector<FakeLaunch>& got, int coll, ar_algo algo, 
 void check_launches(ar_ctx* ctx) {
     std::mt19937_64 rng(12345);
     const ar_algo algos[] = {AR_ALGO_RING_STEP, AR_ALGO_RING_FUSED, AR_ALGO_TREE,
-                             AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE, AR_ALGO_AUTO};
+                             AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE, AR_ALGO_AUTO,
+                             AR_ALGO_TREE_FUSED, AR_ALGO_HALVING_DOUBLING_FUSED};
     const ar_dtype dts[] = {AR_INT32, AR_FLOAT32, AR_BFLOAT16};
     const ar_op ops[] = {AR_SUM, AR_MAX, AR_AVG};
     const size_t special[] = {1, 2, 3, 7, 15, 16, 17, 63, 64, 65, 4095, 4096, 4097, 65536,
@@ -252,7 +263,7 @@ void check_launches(ar_ctx* ctx) {
     int calls = 0;
     for (int iter = 0; iter < 4000; ++iter) {
         const int n = 1 + (int)(rng() % kMaxN);
-        const ar_algo algo = algos[rng() % 6];
+        const ar_algo algo = algos[rng() % (sizeof algos / sizeof algos[0])];
         const int coll = (int)(rng() % 3);
         const ar_dtype dt = dts[rng() % 3];
         ar_op op = ops[rng() % 3];
@@ -269,8 +280,10 @@ void check_launches(ar_ctx* ctx) {
             bufs[r] = rank_addr(r, mixed ? ((size_t)r % (16 / eb)) * eb : shift);
         fake_clear_executed();
         const ar_status st = call(ctx, coll, bufs, n, count, dt, op, algo);
-        const bool tree_only = algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE;
-        const bool needs_pow2 = tree_only || algo == AR_ALGO_HALVING_DOUBLING;
+        const bool tree_only = algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE ||
+                               algo == AR_ALGO_TREE_FUSED;
+        const bool needs_pow2 = tree_only || algo == AR_ALGO_HALVING_DOUBLING ||
+                                algo == AR_ALGO_HALVING_DOUBLING_FUSED;
         char what[160];
         std::snprintf(what, sizeof what, "coll %d algo %d n %d count %zu dtype %d op %d shift %zu%s",
                       coll, (int)algo, n, count, (int)dt, (int)op, shift, mixed ? " mixed" : "");
@@ -301,6 +314,7 @@ void check_launches(ar_ctx* ctx) {
                 p.step = e.step;
                 p.vec = !mixed;
                 p.mis = mixed ? 0u : (unsigned)shift;
+                p.order = order_of(coll, resolved);
                 arlib::Shape sh;
                 fits = fits && arlib::plan_shape(p, &sh);
             }
@@ -319,6 +333,7 @@ void check_launches(ar_ctx* ctx) {
         }
         check_sequence(fake_executed(), coll, resolved, n, count, dt, op, bufs, what);
         for (const FakeLaunch& l : fake_executed()) {
+            CHECK(l.plan.order == order_of(coll, resolved), "%s: fold order %d", what, l.plan.order);
             const bool vec = !mixed;
             CHECK(l.plan.vec == vec, "%s: vec flag", what);
             CHECK(l.plan.mis == (vec ? (unsigned)shift : 0u), "%s: mis %u", what, l.plan.mis);

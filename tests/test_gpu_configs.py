@@ -84,15 +84,13 @@ def test_ddp_bucket_config_full_oracle():
         assert_bits_equal(got, want, algo)
         assert (np.abs(got.astype(np.float64) - f64) <= bound + 2.0 ** -149).all()
     tw = oracle.simulate_tree_allreduce(xs, "float32", "avg").state[0]
-    ts = to_gpu(xs, "float32")
-    run(ts, "avg", "tree")
-    assert ranks_identical(ts)
-    assert_bits_equal(to_np(ts[0]), tw, "tree")
     hw = oracle.simulate_hd_allreduce(xs, "float32", "avg").state[0]
-    ts = to_gpu(xs, "float32")
-    run(ts, "avg", "halving_doubling")
-    assert ranks_identical(ts)
-    assert_bits_equal(to_np(ts[0]), hw, "halving_doubling")
+    for algo, want in (("tree", tw), ("tree_fused", tw), ("halving_doubling", hw),
+                       ("halving_doubling_fused", hw)):
+        ts = to_gpu(xs, "float32")
+        run(ts, "avg", algo)
+        assert ranks_identical(ts)
+        assert_bits_equal(to_np(ts[0]), want, algo)
     dw = oracle.simulate_double_tree_allreduce(xs, "float32", "avg").state[0]
     ts = to_gpu(xs, "float32")
     run(ts, "avg", "double_tree")
@@ -141,14 +139,20 @@ def test_sweep_config(w):
         idx = sample_positions(w.count, w.nranks, k=4096, seed=2)
         vals = gather(a, idx)
     b, c, h, d = clone_all(a), clone_all(a), clone_all(a), clone_all(a)
+    cf, hf = clone_all(a), clone_all(a)
     run(a, "sum", "ring_step")
     run(b, "sum", "ring_fused")
     run(c, "sum", "tree")
     run(h, "sum", "halving_doubling")
     run(d, "sum", "double_tree")
+    run(cf, "sum", "tree_fused")
+    run(hf, "sum", "halving_doubling_fused")
     assert ranks_identical(d)
     for r in range(w.nranks):
         assert torch.equal(a[r], b[r]), f"fused != step on rank {r}"
+        assert torch.equal(c[r], cf[r]), f"tree_fused != tree on rank {r}"
+        assert torch.equal(h[r], hf[r]), f"halving_doubling_fused != halving_doubling on rank {r}"
+    del cf, hf
     assert ranks_identical(a) and ranks_identical(c) and ranks_identical(h)
     if full:
         assert_bits_equal(to_np(a[0]), oracle.simulate_ring_allreduce(xs, "float32", "sum").state[0],

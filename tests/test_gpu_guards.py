@@ -25,7 +25,9 @@ SENTINEL = {"int32": np.int32(0x7BADBEEF),
 
 AR_SIMS = {"ring_step": oracle.simulate_ring_allreduce, "ring_fused": oracle.simulate_ring_allreduce,
            "tree": oracle.simulate_tree_allreduce, "halving_doubling": oracle.simulate_hd_allreduce,
-           "double_tree": oracle.simulate_double_tree_allreduce}
+           "double_tree": oracle.simulate_double_tree_allreduce,
+           "tree_fused": oracle.simulate_tree_allreduce,
+           "halving_doubling_fused": oracle.simulate_hd_allreduce}
 
 
 def _inputs(dtype, n, count, seed):
@@ -72,7 +74,8 @@ CASES = [(8, 1), (8, 7), (8, 1001), (3, 10007), (16, 4099), (64, 130), (64, 70_0
 @pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("bfloat16", "sum"), ("int32", "max")])
 @pytest.mark.parametrize("n,count", CASES)
 def test_allreduce_writes_only_its_buffers(algo, dtype, op, n, count):
-    if algo in ("tree", "halving_doubling", "double_tree") and n & (n - 1):
+    if algo in ("tree", "halving_doubling", "double_tree", "tree_fused",
+                "halving_doubling_fused") and n & (n - 1):
         pytest.skip("needs a power-of-two rank count")
     xs = _inputs(dtype, n, count, seed=n * 613 + count)
     want = AR_SIMS[algo](xs, dtype, op).state
@@ -86,10 +89,11 @@ def test_allreduce_writes_only_its_buffers(algo, dtype, op, n, count):
             assert_bits_equal(to_np(views[r]), want[r], f"{what} rank {r}")
 
 
-@pytest.mark.parametrize("algo", ["ring_step", "ring_fused", "halving_doubling"])
+@pytest.mark.parametrize("algo", ["ring_step", "ring_fused", "halving_doubling",
+                                  "halving_doubling_fused"])
 @pytest.mark.parametrize("n,count", CASES)
 def test_reduce_scatter_and_allgather_write_only_their_buffers(algo, n, count):
-    if algo == "halving_doubling" and n & (n - 1):
+    if algo.startswith("halving_doubling") and n & (n - 1):
         pytest.skip("needs a power-of-two rank count")
     dtype, op = "float32", "sum"
     xs = _inputs(dtype, n, count, seed=n * 919 + count)

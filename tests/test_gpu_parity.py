@@ -294,3 +294,53 @@ def test_fused_many_ranks_small_chunks(dtype, op, n, count):
     for r, (lo, ln) in enumerate(oracle.chunk_layout(count, n)):
         assert_bits_equal(to_np(ts[r])[lo:lo + ln], want[r][lo:lo + ln],
                           f"fused RS {dtype} {op} n={n} count={count} rank {r}")
+
+
+# The one-pass forms of recursive doubling and halving-doubling: same bits as
+# the per-step algorithms (the oracle's message-passing simulations), over
+# every fused shape -- WIDE (8 ranks, 16-byte path), DEEP, TINY (33-64 ranks,
+# small chunks) and the element-wise path (counts below N, bf16 heads).
+POW2 = [(2, 1), (2, 4099), (4, 6), (4, 24581), (8, 1), (8, 1000), (8, 65539), (16, 33),
+        (16, 40003), (32, 2050), (64, 63), (64, 4101), (64, 70_001)]
+FUSED_TREES = [("tree_fused", oracle.simulate_tree_allreduce),
+               ("halving_doubling_fused", oracle.simulate_hd_allreduce)]
+
+
+@pytest.mark.parametrize("algo,sim", FUSED_TREES, ids=[a for a, _ in FUSED_TREES])
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("n,count", POW2)
+def test_fused_tree_orders_match_oracle(algo, sim, dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n * 7207 + count)
+    want = sim(xs, dtype, op).state
+    ts = to_gpu(xs, dtype)
+    ar.allreduce(ts, op=op, algo=algo)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), want[r], f"{algo} {dtype} {op} n={n} count={count} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op", DT_OPS)
+@pytest.mark.parametrize("n,count", POW2)
+def test_fused_halving_doubling_reduce_scatter_then_allgather(dtype, op, n, count):
+    xs = rand_inputs(dtype, n, count, seed=n * 131 + count)
+    rs = oracle.simulate_hd_reduce_scatter(xs, dtype, op).state
+    full = oracle.simulate_hd_allreduce(xs, dtype, op).state
+    ts = to_gpu(xs, dtype)
+    ar.reduce_scatter(ts, op=op, algo="halving_doubling_fused")
+    torch.cuda.synchronize()
+    for r, (lo, ln) in enumerate(oracle.chunk_layout(count, n)):
+        assert_bits_equal(to_np(ts[r])[lo:lo + ln], rs[r][lo:lo + ln], f"RS rank {r}")
+    ar.allgather(ts, algo="halving_doubling_fused")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), full[r], f"RS+AG rank {r}")
+
+
+def test_fused_tree_orders_refuse_what_they_do_not_define():
+    ts = to_gpu(rand_inputs("float32", 6, 100, seed=1), "float32")
+    for algo in ("tree_fused", "halving_doubling_fused"):
+        with pytest.raises(ar.ArError):
+            ar.allreduce(ts, op="sum", algo=algo)           # 6 ranks: not a power of two
+    ts = to_gpu(rand_inputs("float32", 8, 100, seed=1), "float32")
+    with pytest.raises(ar.ArError):
+        ar.reduce_scatter(ts, op="sum", algo="tree_fused")  # AllReduce only
