@@ -44,7 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # the sources the fused kernel and the calibration copy are built from
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_rs_amd", "csrc", f)
                   for f in ("common.h", "elem.h", "launch.h", "fused_impl.h", "fused.hip",
-                            "fused_f32.hip", "fused_bf16.hip", "fused_i32.hip", "copy.hip")]
+                            "fused_f32.hip", "fused_bf16.hip", "fused_i32.hip", "fused_f32_lead.hip",
+                            "fused_bf16_lead.hip", "fused_i32_lead.hip", "copy.hip")]
 
 
 def kernel_source_hash() -> str:

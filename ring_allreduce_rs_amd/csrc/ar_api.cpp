@@ -347,8 +347,16 @@ struct Launch {
 // The kernels of L, in launch order.
 std::vector<arlib::Plan> plans_of(const Launch& L) {
     std::vector<arlib::Plan> ps;
+    // a chunk body can start off a 128-byte line unless rank 0's buffer and
+    // every chunk start are line-aligned (then the fused grid needs no slack)
+    const size_t chunk_bytes = (L.count + (size_t)L.nranks - 1) / (size_t)L.nranks *
+                               (size_t)elem_bytes((ar_dtype)L.dtype);
+    const bool lines = (reinterpret_cast<uintptr_t>(L.t.p[0]) & 127u) == 0 && chunk_bytes % 128 == 0;
     auto add = [&](arlib::Kind k, int st, int order = arlib::ORDER_RING) {
         ps.push_back(make_plan(k, L.dtype, L.op, L.nranks, L.count, st, L.vec, L.mis, order));
+        const bool fused = k == arlib::KIND_FUSED_AR || k == arlib::KIND_FUSED_RS ||
+                           k == arlib::KIND_FUSED_AG;
+        ps.back().lead = fused && L.vec && !lines;
     };
     const arlib::Kind fused = L.coll == COLL_AR   ? arlib::KIND_FUSED_AR
                               : L.coll == COLL_RS ? arlib::KIND_FUSED_RS

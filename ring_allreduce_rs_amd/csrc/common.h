@@ -70,6 +70,7 @@ struct FusedTiny {
 enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_MID = 2, CFG_TINY = 3 };
 #define CFG_MID_VALUE 2   // for the preprocessor: MID kernels exist only when forced
 constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
+constexpr size_t kLeadUnits = 7;    // most idle 16-byte units before a chunk body (128-byte lines)
 // Streaming (non-temporal) loads and stores.  The fused kernel touches every
 // byte once, so caching it only evicts useful lines: on MI355X 8 x 25 MiB went
 // from 86 us to 77 us with both loads and stores streaming.  The per-step
@@ -177,6 +178,10 @@ hipError_t launch_fused_kind(const Plan& p, const Args& a, dim3 grid, hipStream_
 hipError_t launch_fused_i32(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
 hipError_t launch_fused_f32(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
 hipError_t launch_fused_bf16(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+// the same for plans with p.vec && p.lead (line-aligned tiles)
+hipError_t launch_fused_i32_lead(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+hipError_t launch_fused_f32_lead(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
+hipError_t launch_fused_bf16_lead(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
 hipError_t launch_step_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s);
 
 }  // namespace arlib

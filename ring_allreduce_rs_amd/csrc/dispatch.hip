@@ -64,7 +64,8 @@ bool plan_shape(const Plan& p, Shape* out) {
         groups = (size_t)p.nranks;
     } else {
         const size_t per = ceil_div(p.count, (size_t)p.nranks);
-        tiles = ceil_div(ceil_div(per, epu), per_tile);
+        const size_t slack = fused && p.lead && epu > 1 ? kLeadUnits : 0;
+        tiles = ceil_div(ceil_div(per, epu) + slack, per_tile);
         groups = (size_t)p.nranks;
     }
     if (tiles == 0) tiles = 1;

@@ -7,7 +7,10 @@ namespace arlib {
 template <int EB>
 static hipError_t launch_fused_ag(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
     const dim3 block(kFusedThreads);
-    if (p.vec)
+    if (p.vec && p.lead)
+        hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 0, FusedWide, ORDER_RING, true>),
+                           grid, block, 0, s, a);
+    else if (p.vec)
         hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 0, FusedWide>), grid, block, 0,
                            s, a);
     else

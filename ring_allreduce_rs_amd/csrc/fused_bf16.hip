@@ -5,6 +5,7 @@
 namespace arlib {
 
 hipError_t launch_fused_bf16(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
+    if (use_lead(p)) return launch_fused_bf16_lead(p, a, grid, s);
     return p.op == AR_MAX ? launch_fused_op<OpBF16Max>(p, a, grid, s)
                           : launch_fused_op<OpBF16Sum>(p, a, grid, s);
 }

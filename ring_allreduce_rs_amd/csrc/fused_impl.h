@@ -31,9 +31,10 @@ namespace arlib {
 // arguments.
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
-template <class Op, int MODE, bool VEC, int NR, class CFG, int ORDER = ORDER_RING>
+template <class Op, int MODE, bool VEC, int NR, class CFG, int ORDER = ORDER_RING,
+          bool LEAD = false>
 __device__ __forceinline__ void fused_units(const Args& a, int c, int start, size_t byte0,
-                                            size_t ubase, size_t units) {
+                                            size_t ubase, size_t units, unsigned lead = 0) {
     using X = Unit<Op, VEC, kFusedNT>;
     using T = typename X::T;
     constexpr int U = CFG::U;
@@ -43,7 +44,9 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
     size_t off[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const size_t idx = ubase + (size_t)u * kFusedThreads;
+        // slot ubase + u*threads of the tile grid is unit (slot - lead) of the
+        // body; a slot before the body wraps to a huge idx and fails the test
+        const size_t idx = ubase + (size_t)u * kFusedThreads - (LEAD ? lead : 0u);
         ok[u] = idx < units;
         off[u] = byte0 + idx * X::kBytes;
     }
@@ -174,7 +177,11 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
     }
 }
 
-template <class Op, int MODE, bool VEC, int NR, class CFG, int ORDER = ORDER_RING>
+// LEAD: tiles start on 128-byte lines (see below); launched only for plans
+// whose chunk bodies can start off a line, so the aligned case keeps the
+// plain indexing.
+template <class Op, int MODE, bool VEC, int NR, class CFG, int ORDER = ORDER_RING,
+          bool LEAD = false>
 __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
     constexpr int EB = Op::kElemBytes;
     const int n = NR > 0 ? NR : a.n;
@@ -185,9 +192,18 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
     if (len == 0) return;
     const Span sp = make_span<EB, VEC>(lo, len, a.mis);
     const int start = (c + 1 == n) ? 0 : c + 1;
+    // Tiles start on a 128-byte line of rank 0's buffer: a body starting
+    // `lead` units past a line leaves the first `lead` slots of tile 0 idle,
+    // so no wave access straddles a line that the next tile touches again.
+    // The host sizes the grid for that slack whenever a lead can occur.
+    const unsigned lead =
+        VEC && LEAD
+            ? (unsigned)(((reinterpret_cast<uintptr_t>(a.t.p[0]) + sp.body * EB) & 127u) >> 4)
+            : 0u;
     const size_t ubase = (size_t)tile * (kFusedThreads * CFG::U) + threadIdx.x;
-    if (ubase < sp.units)
-        fused_units<Op, MODE, VEC, NR, CFG, ORDER>(a, c, start, sp.body * EB, ubase, sp.units);
+    if (ubase < sp.units + lead)
+        fused_units<Op, MODE, VEC, NR, CFG, ORDER, LEAD>(a, c, start, sp.body * EB, ubase,
+                                                         sp.units, lead);
     if constexpr (VEC) {
         // heads have at most 15 bytes (< 8 elements), as do tails
         if (tile == 0) {
@@ -202,53 +218,72 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
     }
 }
 
-template <class Op, int MODE, bool VEC, int ORDER>
+// Which indexing a 16-byte-path plan runs with.  The line-aligned (LEAD)
+// kernels are needed whenever a chunk body can start off a 128-byte line
+// (p.lead).  On line-aligned layouts both forms are correct; measured on
+// MI355X the LEAD forms ran 0.5-2.8 % faster there on the DEEP and run-time-N
+// WIDE shapes, and 3.7 % slower on the 8-rank WIDE kernel, which therefore
+// keeps the plain indexing when the layout allows it.
+inline bool use_lead(const Plan& p) {
+    const bool n8_wide = AR_SPECIALIZE_N && p.nranks == 8 && fused_variant(p) == CFG_WIDE;
+    return p.vec && (p.lead || !n8_wide);
+}
+
+template <class Op, int MODE, bool VEC, int ORDER, bool LEAD = false>
 inline hipError_t launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
     const dim3 block(kFusedThreads);
     const int cfg = fused_variant(p);
     const bool n8 = AR_SPECIALIZE_N && VEC && p.nranks == 8;
-    if (cfg == CFG_TINY) {
+    if constexpr (VEC && !LEAD) {
+        // plain 16-byte indexing: the aligned 8-rank WIDE kernel only (use_lead)
+        if (!n8 || cfg != CFG_WIDE) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedWide, ORDER>), grid, block, 0, s, a);
+    } else if (cfg == CFG_TINY) {
         // element-wise units whatever the alignment (the grid was sized so)
         hipLaunchKernelGGL((k_fused<Op, MODE, false, 0, FusedTiny, ORDER>), grid, block, 0, s, a);
     } else if (cfg == CFG_DEEP) {
         // the runtime-N loop measured faster than the 8-rank unrolled one here
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep, ORDER>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep, ORDER, LEAD>), grid, block, 0, s, a);
 #if AR_FUSED_FORCE_CFG == CFG_MID_VALUE
     } else if (cfg == CFG_MID) {
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedMid, ORDER>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedMid, ORDER, LEAD>), grid, block, 0, s, a);
 #endif
     } else if (n8) {
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide, ORDER>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide, ORDER, LEAD>), grid, block, 0, s, a);
     } else if constexpr (ORDER == ORDER_RING) {
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedWide>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedWide, ORDER_RING, LEAD>), grid, block, 0, s, a);
     } else {
         return hipErrorInvalidConfiguration;   // no such kernel (fused_variant never asks)
     }
     return hipSuccess;
 }
 
-template <class Op, int MODE, int ORDER>
+// LEAD selects the line-aligned instantiations (16-byte path only); the
+// per-type files compile them in translation units of their own.
+template <class Op, int MODE, int ORDER, bool LEAD>
 inline hipError_t launch_fused_v(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
-    return p.vec ? launch_fused_n<Op, MODE, true, ORDER>(p, a, grid, s)
-                 : launch_fused_n<Op, MODE, false, ORDER>(p, a, grid, s);
+    if constexpr (LEAD) return launch_fused_n<Op, MODE, true, ORDER, true>(p, a, grid, s);
+    else
+        return p.vec ? launch_fused_n<Op, MODE, true, ORDER>(p, a, grid, s)
+                     : launch_fused_n<Op, MODE, false, ORDER>(p, a, grid, s);
 }
 
-template <class Op>
+template <class Op, bool LEAD = false>
 inline hipError_t launch_fused_op(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
     const bool rs = p.kind == KIND_FUSED_RS;
     if (p.kind != KIND_FUSED_AR && !rs) return hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     switch (p.order) {
         case ORDER_RING:
-            e = rs ? launch_fused_v<Op, KIND_FUSED_RS, ORDER_RING>(p, a, grid, s)
-                   : launch_fused_v<Op, KIND_FUSED_AR, ORDER_RING>(p, a, grid, s);
+            e = rs ? launch_fused_v<Op, KIND_FUSED_RS, ORDER_RING, LEAD>(p, a, grid, s)
+                   : launch_fused_v<Op, KIND_FUSED_AR, ORDER_RING, LEAD>(p, a, grid, s);
             break;
         case ORDER_PAIR:   // recursive doubling: AllReduce only
-            if (!rs) e = launch_fused_v<Op, KIND_FUSED_AR, ORDER_PAIR>(p, a, grid, s);
+            if (!rs) e = launch_fused_v<Op, KIND_FUSED_AR, ORDER_PAIR, LEAD>(p, a, grid, s);
             break;
         case ORDER_PAIR_BITREV:
-            e = rs ? launch_fused_v<Op, KIND_FUSED_RS, ORDER_PAIR_BITREV>(p, a, grid, s)
-                   : launch_fused_v<Op, KIND_FUSED_AR, ORDER_PAIR_BITREV>(p, a, grid, s);
+            e = rs ? launch_fused_v<Op, KIND_FUSED_RS, ORDER_PAIR_BITREV, LEAD>(p, a, grid, s)
+                   : launch_fused_v<Op, KIND_FUSED_AR, ORDER_PAIR_BITREV, LEAD>(p, a, grid, s);
             break;
         default:
             break;

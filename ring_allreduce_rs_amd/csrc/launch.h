@@ -46,6 +46,10 @@ struct Plan {
     bool vec;           // 16-byte path (all buffers share their address mod 16)
     unsigned mis;       // that common address mod 16, in bytes
     int order = ORDER_RING;   // fold order of the fused kinds (Order)
+    // Fused kinds: some chunk body may start off a 128-byte line of rank 0's
+    // buffer.  The kernel then shifts its tiles back to the line (up to 7 idle
+    // 16-byte units at the front) and the grid carries that slack.
+    bool lead = false;
 };
 
 // Grid / block shape a plan launches with (for logging and tests).

@@ -315,6 +315,11 @@ void check_launches(ar_ctx* ctx) {
                 p.vec = !mixed;
                 p.mis = mixed ? 0u : (unsigned)shift;
                 p.order = order_of(coll, resolved);
+                const size_t cb = (count + (size_t)n - 1) / (size_t)n * eb;
+                const bool fused_kind = e.kind == arlib::KIND_FUSED_AR ||
+                                        e.kind == arlib::KIND_FUSED_RS || e.kind == arlib::KIND_FUSED_AG;
+                p.lead = fused_kind && p.vec &&
+                         !((reinterpret_cast<uintptr_t>(bufs[0]) & 127u) == 0 && cb % 128 == 0);
                 arlib::Shape sh;
                 fits = fits && arlib::plan_shape(p, &sh);
             }
@@ -332,11 +337,18 @@ void check_launches(ar_ctx* ctx) {
             continue;
         }
         check_sequence(fake_executed(), coll, resolved, n, count, dt, op, bufs, what);
+        const bool lines = (reinterpret_cast<uintptr_t>(bufs[0]) & 127u) == 0 &&
+                           (count + (size_t)n - 1) / (size_t)n * eb % 128 == 0;
         for (const FakeLaunch& l : fake_executed()) {
             CHECK(l.plan.order == order_of(coll, resolved), "%s: fold order %d", what, l.plan.order);
             const bool vec = !mixed;
             CHECK(l.plan.vec == vec, "%s: vec flag", what);
             CHECK(l.plan.mis == (vec ? (unsigned)shift : 0u), "%s: mis %u", what, l.plan.mis);
+            const bool fused_kind = l.plan.kind == arlib::KIND_FUSED_AR ||
+                                    l.plan.kind == arlib::KIND_FUSED_RS ||
+                                    l.plan.kind == arlib::KIND_FUSED_AG;
+            CHECK(l.plan.lead == (fused_kind && vec && !lines), "%s: lead flag %d", what,
+                  (int)l.plan.lead);
         }
     }
     CHECK(calls > 1000, "too few accepted calls (%d)", calls);

@@ -129,11 +129,14 @@ void record(const arlib::Plan& p, const arlib::Args& a, dim3 grid, hipStream_t s
         upl = arlib::kUnroll;
         epu = p.vec ? 16 / eb : 1;
     }
+    // a fused plan whose chunk bodies can start off a 128-byte line shifts its
+    // tiles back by up to kLeadUnits idle units: the grid must cover those too
+    const size_t lead = fused && p.lead && epu > 1 ? arlib::kLeadUnits * epu : 0;
     if (a.tiles == 0 || (size_t)grid.x != (size_t)a.tiles * groups)
         coverage_fail("grid is not tiles x groups", a, grid);
-    else if ((size_t)a.tiles * threads * upl * epu < elems)
+    else if ((size_t)a.tiles * threads * upl * epu < elems + lead)
         coverage_fail("tiles do not cover the group's elements", a, grid);
-    else if (elems > 0 && ((size_t)a.tiles - 1) * threads * upl * epu >= elems + threads * upl * epu)
+    else if (elems > 0 && ((size_t)a.tiles - 1) * threads * upl * epu >= elems + lead + threads * upl * epu)
         coverage_fail("more tiles than the work needs", a, grid);
     if (a.n != p.nranks || a.count != p.count || a.per != (p.count + p.nranks - 1) / p.nranks)
         coverage_fail("kernel arguments disagree with the plan", a, grid);

@@ -344,3 +344,54 @@ def test_fused_tree_orders_refuse_what_they_do_not_define():
     ts = to_gpu(rand_inputs("float32", 8, 100, seed=1), "float32")
     with pytest.raises(ar.ArError):
         ar.reduce_scatter(ts, op="sum", algo="tree_fused")  # AllReduce only
+
+
+# Chunk bodies that start off a 128-byte line take the line-aligned kernels
+# (tiles shifted back by 0-7 idle 16-byte units).  Rank 0's view walks
+# through one line in 16-byte steps (every shift value); the counts make the
+# chunk starts themselves drift across lines and span several tiles per chunk
+# (WIDE tile: 4 KiB per rank; DEEP: 1 KiB).
+LINE_CASES = [(3, 3 * 4099 + 1), (8, 8 * 2051 + 5), (16, 16 * 3001 + 7)]
+
+
+@pytest.mark.parametrize("dtype,op", [("float32", "avg"), ("int32", "sum"), ("bfloat16", "sum"),
+                                      ("float32", "max")])
+@pytest.mark.parametrize("n,count", LINE_CASES)
+@pytest.mark.parametrize("line_shift", [0, 16, 48, 112])
+def test_line_aligned_tiles_match_oracle(dtype, op, n, count, line_shift):
+    xs = rand_inputs(dtype, n, count, seed=n * 977 + line_shift)
+    eb = 2 if dtype == "bfloat16" else 4
+    shift = line_shift // eb                      # elements; a multiple of 16 bytes
+    stride = ((count + 256) // 64 + 1) * 64       # rows of whole 128-byte lines (fp32)
+    tdt = to_gpu(xs[:1], dtype)[0].dtype
+    want_ring = oracle.simulate_ring_allreduce(xs, dtype, op).state
+    rs_want = oracle.simulate_ring_reduce_scatter(xs, dtype, op).state
+    algos = [("ring_fused", want_ring)]
+    if n & (n - 1) == 0:
+        algos += [("tree_fused", oracle.simulate_tree_allreduce(xs, dtype, op).state),
+                  ("halving_doubling_fused", oracle.simulate_hd_allreduce(xs, dtype, op).state)]
+    for algo, want in algos + [("rs+ag", want_ring)]:
+        store = torch.zeros(n * stride + 64, dtype=tdt, device="cuda")
+        assert store.data_ptr() % 128 == 0
+        views = []
+        for r in range(n):
+            v = store[r * stride + shift:r * stride + shift + count]
+            v.copy_(to_gpu([xs[r]], dtype)[0])
+            views.append(v)
+        guard = store.clone()
+        if algo == "rs+ag":
+            ar.reduce_scatter(views, op=op, algo="ring_fused")
+            torch.cuda.synchronize()
+            for r, (lo, ln) in enumerate(oracle.chunk_layout(count, n)):
+                assert_bits_equal(to_np(views[r])[lo:lo + ln], rs_want[r][lo:lo + ln],
+                                  f"RS shift {line_shift} rank {r}")
+            ar.allgather(views, algo="ring_fused")
+        else:
+            ar.allreduce(views, op=op, algo=algo)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(views[r]), want[r], f"{algo} shift {line_shift} rank {r}")
+        mask = torch.ones_like(store, dtype=torch.bool)
+        for r in range(n):
+            mask[r * stride + shift:r * stride + shift + count] = False
+        assert torch.equal(store[mask], guard[mask]), f"{algo}: wrote outside the rank views"
