@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import ring_allreduce_rs_amd as ar
-from tests.gpu_helpers import assert_bits_equal, to_gpu, to_np
+from tests.gpu_helpers import TORCH_DT, assert_bits_equal, to_gpu, to_np
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -395,3 +395,59 @@ def test_line_aligned_tiles_match_oracle(dtype, op, n, count, line_shift):
         for r in range(n):
             mask[r * stride + shift:r * stride + shift + count] = False
         assert torch.equal(store[mask], guard[mask]), f"{algo}: wrote outside the rank views"
+
+
+# Seeded random layouts: rank counts 1-64, counts from 0 up to a few tiles per
+# chunk, every dtype/op, a common shift of rank 0's row within a 128-byte line
+# (16-byte path, with or without line-aligned tiles) or mixed per-rank shifts
+# (element-wise path).  One-pass AllReduce, and ReduceScatter then AllGather,
+# bitwise against the oracle, with nothing written outside the views.
+def _random_layout_cases(k=40, seed=20261203):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(k):
+        n = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 31, 64]))
+        dtype, op = DT_OPS[int(rng.integers(len(DT_OPS)))]
+        count = int(rng.choice([0, 1, n - 1, n * 1000 + 3, int(rng.integers(1, 40000))]))
+        mixed = bool(rng.integers(4) == 0)
+        shift_bytes = int(rng.integers(0, 128))
+        out.append((i, n, max(count, 0), dtype, op, mixed, shift_bytes))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_layout_cases(), ids=lambda c: f"case{c[0]}")
+def test_random_layouts_match_oracle(case):
+    _, n, count, dtype, op, mixed, shift_bytes = case
+    eb = 2 if dtype == "bfloat16" else 4
+    xs = rand_inputs(dtype, n, count, seed=case[0] + 5000)
+    want = oracle.simulate_ring_allreduce(xs, dtype, op).state
+    rs_want = oracle.simulate_ring_reduce_scatter(xs, dtype, op).state
+    stride = ((count + 512) // 64 + 1) * 64           # whole 128-byte lines per row
+    base_shift = shift_bytes // eb
+    shifts = [(base_shift + (r % 3 if mixed else 0)) for r in range(n)]
+    tdt = TORCH_DT[dtype]
+    for kind in ("allreduce", "rs+ag"):
+        store = torch.zeros(n * stride + 64, dtype=tdt, device="cuda")
+        views = []
+        for r in range(n):
+            v = store[r * stride + shifts[r]:r * stride + shifts[r] + count]
+            if count:
+                v.copy_(to_gpu([xs[r]], dtype)[0])
+            views.append(v)
+        guard = store.clone()
+        if kind == "allreduce":
+            ar.allreduce(views, op=op, algo="ring_fused")
+        else:
+            ar.reduce_scatter(views, op=op, algo="ring_fused")
+            torch.cuda.synchronize()
+            for r, (lo, ln) in enumerate(oracle.chunk_layout(count, n)):
+                assert_bits_equal(to_np(views[r])[lo:lo + ln], rs_want[r][lo:lo + ln],
+                                  f"RS {case} rank {r}")
+            ar.allgather(views, algo="ring_fused")
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits_equal(to_np(views[r]), want[r], f"{kind} {case} rank {r}")
+        mask = torch.ones_like(store, dtype=torch.bool)
+        for r in range(n):
+            mask[r * stride + shifts[r]:r * stride + shifts[r] + count] = False
+        assert torch.equal(store[mask], guard[mask]), f"{kind} {case}: wrote outside the views"
