@@ -165,6 +165,14 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
             for (int u = 0; u < U; ++u)
                 if (ok[u]) X::st(dst + off[u], acc[u]);
         } else {
+            if constexpr (ORDER != ORDER_RING) {
+                // The pairwise orders load ranks in index order, the order of
+                // these stores; hiding the offsets stops the compiler from
+                // keeping every load address alive for reuse here (56 more
+                // VGPRs, one wave per SIMD fewer).  Recomputing them is cheap.
+#pragma unroll
+                for (int u = 0; u < U; ++u) asm volatile("" : "+v"(off[u]));
+            }
 #pragma unroll
             for (int r2 = 0; r2 < (NR > 0 ? NR : AR_MAX_RANKS); ++r2) {
                 if (NR == 0 && r2 >= n) break;
