@@ -165,11 +165,13 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
             for (int u = 0; u < U; ++u)
                 if (ok[u]) X::st(dst + off[u], acc[u]);
         } else {
-            if constexpr (ORDER != ORDER_RING) {
-                // The pairwise orders load ranks in index order, the order of
-                // these stores; hiding the offsets stops the compiler from
-                // keeping every load address alive for reuse here (56 more
-                // VGPRs, one wave per SIMD fewer).  Recomputing them is cheap.
+            if constexpr (ORDER != ORDER_RING || NR == 0) {
+                // Hiding the offsets stops the compiler from keeping the load
+                // addresses alive across the fold for reuse by these stores
+                // (the pairwise orders load ranks in the stores' order: 56
+                // more VGPRs; the run-time-N fp32 MAX loop: 17 more), which
+                // costs a wave per SIMD.  Recomputing them is cheap.  The
+                // 8-rank ring kernel does not reuse them and is left as is.
 #pragma unroll
                 for (int u = 0; u < U; ++u) asm volatile("" : "+v"(off[u]));
             }
