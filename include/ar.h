@@ -29,6 +29,12 @@
  *  - No C++ exception crosses this interface.  A context is not thread-safe;
  *    use one per host thread / stream.
  *  - ar_last_error(ctx) describes the most recent failure on that context.
+ *  - Alignment and speed: any element-aligned address is accepted.  Buffers
+ *    that share their address modulo 16 take the 16-byte path (element-wise
+ *    heads and tails per chunk); otherwise the whole call runs element by
+ *    element.  On the 16-byte path, chunks whose bodies start off a 128-byte
+ *    line of bufs[0] have their tiles shifted onto lines, so they move no
+ *    more bytes than aligned ones.
  *  - The device-memory check of bufs (device, type, extent inside the
  *    allocation) is cached per context for the 32 most recent pointer sets;
  *    a buffer freed and re-allocated smaller at the same address between two
