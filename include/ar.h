@@ -67,8 +67,8 @@ typedef enum ar_status AR_ENUM_INT {
     AR_ERR_INVALID_ARG = 1,   /* bad pointer, size, enum, overlap, step index */
     AR_ERR_UNSUPPORTED = 2,   /* valid but not defined: int32 AVG, the tree algorithms
                                  (TREE, HALVING_DOUBLING, DOUBLE_TREE and their fused forms)
-                                 on non-power-of-two N, TREE / TREE_FUSED / DOUBLE_TREE on
-                                 ReduceScatter / AllGather */
+                                 on non-power-of-two N, TREE / TREE_FUSED / DOUBLE_TREE /
+                                 DOUBLE_TREE_FUSED on ReduceScatter / AllGather */
     AR_ERR_RUNTIME = 3,       /* the HIP runtime reported an error */
     AR_ERR_NO_MEMORY = 4      /* host allocation of the context failed */
 } ar_status;
@@ -125,12 +125,18 @@ typedef enum ar_op AR_ENUM_INT { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
  *                (partners at distance N/2 first).  Power-of-two N;
  *                AllReduce, ReduceScatter (owner chunk written) and AllGather
  *                (a copy, as for every algorithm).
+ *  DOUBLE_TREE_FUSED -- the DOUBLE_TREE result (same bits) in one pass: the
+ *                two trees run side by side, every element of each half read
+ *                once from each rank, folded in its tree's in-order order in
+ *                registers, and written to all N ranks (N*K read + N*K
+ *                written).  Power-of-two N; AllReduce only.
  *  AUTO       -- pick the algorithm with the smallest predicted time under the
  *                latency/bandwidth model of ar_predict_us (the pages' size-based
  *                choice between ring and tree: "AllReduce", compassingai.com,
- *                sections 4-5; xdnf.cn page, section 4.3).  On one GPU the fused
- *                pass needs one launch and the fewest bytes, so the model picks
- *                RING_FUSED at every size measured. */
+ *                sections 4-5; xdnf.cn page, section 4.3).  On one GPU a
+ *                one-pass form needs one launch and the fewest bytes; the model
+ *                gives every one-pass form the same time, ties go to
+ *                RING_FUSED, so AUTO picks RING_FUSED at every size measured. */
 typedef enum ar_algo AR_ENUM_INT {
     AR_ALGO_RING_STEP = 0,
     AR_ALGO_RING_FUSED = 1,
@@ -139,7 +145,8 @@ typedef enum ar_algo AR_ENUM_INT {
     AR_ALGO_AUTO = 4,
     AR_ALGO_DOUBLE_TREE = 5,
     AR_ALGO_TREE_FUSED = 6,
-    AR_ALGO_HALVING_DOUBLING_FUSED = 7
+    AR_ALGO_HALVING_DOUBLING_FUSED = 7,
+    AR_ALGO_DOUBLE_TREE_FUSED = 8
 } ar_algo;
 
 /* Create a context bound to HIP device `device` and stream `stream`
@@ -195,8 +202,11 @@ ar_status ar_allreduce(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
 ar_status ar_reduce_scatter(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
                             ar_dtype dtype, ar_op op, ar_algo algo);
 
-/* AllGather in place: chunk r of bufs[r] is copied, bit for bit, into chunk r
- * of every other buffer.  ar_reduce_scatter then ar_allgather with the same
+/* AllGather in place ("AllReduce 集合通信", zzmblog.top, section 语义: every
+ * process ends with every process's shard, assembled in rank order; the ring
+ * runs it as N-1 forwarding steps without accumulation, section 两阶段流程):
+ * chunk r of bufs[r] is copied, bit for bit, into chunk r of every other
+ * buffer.  ar_reduce_scatter then ar_allgather with the same
  * algo equals ar_allreduce bitwise.  RING_STEP, RING_FUSED or
  * HALVING_DOUBLING. */
 ar_status ar_allgather(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
@@ -242,8 +252,13 @@ ar_status ar_hd_ag_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
 ar_status ar_dtree_step(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
                         ar_dtype dtype, ar_op op, int step);
 
-/* Chunk c's element range (host-only; touches no GPU).  Errors: nranks out of
- * range, chunk outside [0, nranks), NULL outputs -> AR_ERR_INVALID_ARG. */
+/* Chunk c's element range (host-only; touches no GPU).  The ring splits each
+ * rank's data into N chunks ("AllReduce", compassingai.com, section 3 技术原理;
+ * pwwt.cn page, section 2.2) and says nothing of counts that N does not
+ * divide; the reading here is a ceiling split: L = ceil(count / N), chunk c =
+ * [min(c*L, count), min((c+1)*L, count)), so trailing chunks are short or
+ * empty.  Exact for every count up to SIZE_MAX.  Errors: nranks out of range,
+ * chunk outside [0, nranks), NULL outputs -> AR_ERR_INVALID_ARG. */
 ar_status ar_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* len);
 
 /* Predicted time in microseconds of one ar_allreduce with `algo` (not AUTO),
@@ -264,6 +279,22 @@ ar_status ar_auto_algo(int nranks, size_t count, ar_dtype dtype, ar_algo* out);
  * size), used to calibrate bandwidth and hardware byte counters against a
  * kernel of known traffic.  Enqueued on the context's stream. */
 ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes);
+
+/* Calibration stream with the fused AllReduce kernel's memory pattern and no
+ * reduction: reads `bytes` bytes from each of the nsrc buffers src[0..nsrc)
+ * and writes their bitwise XOR (zeros when nsrc == 0) to each of the ndst
+ * buffers dst[0..ndst), with the fused kernel's tiling (one 64-lane wave per
+ * block, 4 KiB of every buffer per block, 8 sources of loads in flight,
+ * streaming loads and stores).  nsrc = ndst = N is the ceiling of an N-rank
+ * fused AllReduce's N*K-read / N*K-written pattern on this hardware; other
+ * mixes separate the cost of read streams from that of write streams.
+ * src and dst are HOST arrays of DEVICE pointers (read during the call),
+ * every buffer 16-byte aligned, device memory of the context's device, no two
+ * overlapping; bytes a multiple of 16; 1 <= nsrc + ndst <= AR_MAX_RANKS.
+ * Enqueued on the context's stream.  Errors: AR_ERR_INVALID_ARG for any of
+ * the above, AR_ERR_RUNTIME if the launch fails. */
+ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* dst, int ndst,
+                    size_t bytes);
 
 /* Static description of a status code (never NULL). */
 const char* ar_status_string(ar_status s);

@@ -24,7 +24,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
-    "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "dtree_step", "copy_", "chunk_range", "bind",
+    "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "dtree_step", "copy_", "stream_",
+    "chunk_range", "bind",
     "context", "LIB_PATH", "predict_us", "auto_algo", "set_graphs",
 ]
 
@@ -151,6 +152,21 @@ def copy_(dst, src):
         raise ValueError("copy_ needs equal byte sizes")
     context(src.device.index or 0).copy_ptrs(dst.data_ptr(), src.data_ptr(), nbytes)
     return dst
+
+
+def stream_(srcs, dsts):
+    """Calibration stream (ar_stream): the XOR of the source tensors written to
+    every destination tensor, all of one byte size, on the current stream."""
+    bufs = list(srcs) + list(dsts)
+    if not bufs:
+        raise ValueError("stream_ needs at least one buffer")
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    for t in bufs:
+        if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
+            raise ValueError("stream_ needs contiguous buffers of one byte size")
+    context(bufs[0].device.index or 0).stream_ptrs([t.data_ptr() for t in srcs],
+                                                  [t.data_ptr() for t in dsts], nbytes)
+    return list(dsts)
 
 
 class _Bound:

@@ -25,7 +25,7 @@ AR_ERR_NO_MEMORY = 4
 DTYPES = {"int32": 0, "float32": 1, "bfloat16": 2}
 OPS = {"sum": 0, "max": 1, "avg": 2}
 ALGOS = {"ring_step": 0, "ring_fused": 1, "tree": 2, "halving_doubling": 3, "auto": 4,
-         "double_tree": 5, "tree_fused": 6, "halving_doubling_fused": 7}
+         "double_tree": 5, "tree_fused": 6, "halving_doubling_fused": 7, "double_tree_fused": 8}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 # every symbol include/ar.h declares
@@ -33,7 +33,7 @@ EXPORTS = (
     "ar_create", "ar_set_stream", "ar_set_graphs", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
     "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
     "ar_dtree_step",
-    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy",
+    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy", "ar_stream",
     "ar_status_string", "ar_last_error", "ar_destroy",
 )
 
@@ -80,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "ar_predict_us": ([i, i, sz, i, ctypes.POINTER(ctypes.c_double)], i),
         "ar_auto_algo": ([i, sz, i, ctypes.POINTER(i)], i),
         "ar_copy": ([vp, vp, vp, sz], i),
+        "ar_stream": ([vp, pp, i, pp, i, sz], i),
         "ar_status_string": ([i], cp),
         "ar_last_error": ([vp], cp),
         "ar_destroy": ([vp], i),
@@ -207,6 +208,10 @@ class Context:
 
     def copy_ptrs(self, dst, src, nbytes):
         self._check(lib.ar_copy(self._h, dst, src, nbytes), "ar_copy")
+
+    def stream_ptrs(self, srcs, dsts, nbytes):
+        self._check(lib.ar_stream(self._h, _ptr_array(srcs), len(srcs), _ptr_array(dsts),
+                                  len(dsts), nbytes), "ar_stream")
 
     def close(self) -> None:
         if self._h:

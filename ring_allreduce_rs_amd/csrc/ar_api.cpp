@@ -89,15 +89,17 @@ size_t elem_bytes(ar_dtype d) { return d == AR_BFLOAT16 ? 2 : 4; }
 
 bool valid_dtype(int d) { return d == AR_INT32 || d == AR_FLOAT32 || d == AR_BFLOAT16; }
 bool valid_op(int o) { return o == AR_SUM || o == AR_MAX || o == AR_AVG; }
-bool valid_algo(int a) { return a >= AR_ALGO_RING_STEP && a <= AR_ALGO_HALVING_DOUBLING_FUSED; }
+bool valid_algo(int a) { return a >= AR_ALGO_RING_STEP && a <= AR_ALGO_DOUBLE_TREE_FUSED; }
 // algorithms defined for power-of-two rank counts only
 bool needs_pow2(int a) {
     return a == AR_ALGO_TREE || a == AR_ALGO_HALVING_DOUBLING || a == AR_ALGO_DOUBLE_TREE ||
-           a == AR_ALGO_TREE_FUSED || a == AR_ALGO_HALVING_DOUBLING_FUSED;
+           a == AR_ALGO_TREE_FUSED || a == AR_ALGO_HALVING_DOUBLING_FUSED ||
+           a == AR_ALGO_DOUBLE_TREE_FUSED;
 }
 // algorithms that exist as AllReduce only
 bool allreduce_only(int a) {
-    return a == AR_ALGO_TREE || a == AR_ALGO_DOUBLE_TREE || a == AR_ALGO_TREE_FUSED;
+    return a == AR_ALGO_TREE || a == AR_ALGO_DOUBLE_TREE || a == AR_ALGO_TREE_FUSED ||
+           a == AR_ALGO_DOUBLE_TREE_FUSED;
 }
 int log2_exact(int n) {
     int l = 0;
@@ -156,6 +158,7 @@ double predict_allreduce_us(int algo, int n, size_t count, size_t eb) {
         case AR_ALGO_RING_FUSED:
         case AR_ALGO_TREE_FUSED:
         case AR_ALGO_HALVING_DOUBLING_FUSED:
+        case AR_ALGO_DOUBLE_TREE_FUSED:
             return kCallUs + 2.0 * n * k / (fused_gbps(n) * 1e3);
         case AR_ALGO_RING_STEP:
             return kCallUs + (2.0 * (n - 1) - 1) * kLaunchUs + 5.0 * (n - 1) * k / (kStepGBps * 1e3);
@@ -175,10 +178,16 @@ double predict_allreduce_us(int algo, int n, size_t count, size_t eb) {
     return 1e300;
 }
 
+// The argmin over every algorithm; ties keep the earlier candidate.  The
+// one-pass forms share one prediction (one launch, 2NK bytes), so the fused
+// ring, listed first, takes every tie: on MI355X the one-pass tree orders
+// measured within 3 % of it either way, less than the spread between boxes.
 int auto_algo(int n, size_t count, size_t eb) {
     int best = AR_ALGO_RING_FUSED;
     double best_us = predict_allreduce_us(best, n, count, eb);
-    const int cands[] = {AR_ALGO_RING_STEP, AR_ALGO_HALVING_DOUBLING, AR_ALGO_TREE,
+    const int cands[] = {AR_ALGO_TREE_FUSED,       AR_ALGO_HALVING_DOUBLING_FUSED,
+                         AR_ALGO_DOUBLE_TREE_FUSED, AR_ALGO_RING_STEP,
+                         AR_ALGO_HALVING_DOUBLING, AR_ALGO_TREE,
                          AR_ALGO_DOUBLE_TREE};
     for (int a : cands) {
         if (a != AR_ALGO_RING_STEP && !pow2(n)) continue;
@@ -349,8 +358,9 @@ std::vector<arlib::Plan> plans_of(const Launch& L) {
     std::vector<arlib::Plan> ps;
     // a chunk body can start off a 128-byte line unless rank 0's buffer and
     // every chunk start are line-aligned (then the fused grid needs no slack)
-    const size_t chunk_bytes = (L.count + (size_t)L.nranks - 1) / (size_t)L.nranks *
-                               (size_t)elem_bytes((ar_dtype)L.dtype);
+    const size_t parts = (size_t)arlib::fused_parts(
+        L.algo == AR_ALGO_DOUBLE_TREE_FUSED ? arlib::ORDER_DTREE : arlib::ORDER_RING, L.nranks);
+    const size_t chunk_bytes = (L.count + parts - 1) / parts * (size_t)elem_bytes((ar_dtype)L.dtype);
     const bool lines = (reinterpret_cast<uintptr_t>(L.t.p[0]) & 127u) == 0 && chunk_bytes % 128 == 0;
     auto add = [&](arlib::Kind k, int st, int order = arlib::ORDER_RING) {
         ps.push_back(make_plan(k, L.dtype, L.op, L.nranks, L.count, st, L.vec, L.mis, order));
@@ -373,6 +383,9 @@ std::vector<arlib::Plan> plans_of(const Launch& L) {
         case AR_ALGO_HALVING_DOUBLING_FUSED:
             // the AllGather half is a copy, whatever the order
             add(fused, 0, L.coll == COLL_AG ? arlib::ORDER_RING : arlib::ORDER_PAIR_BITREV);
+            break;
+        case AR_ALGO_DOUBLE_TREE_FUSED:
+            add(fused, 0, arlib::ORDER_DTREE);
             break;
         case AR_ALGO_HALVING_DOUBLING:
             if (rs) for (int st = 0; st < levels; ++st) add(arlib::KIND_HD_RS_STEP, st);
@@ -557,7 +570,8 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
         }
         if (allreduce_only(algo) && coll != COLL_AR)
             return fail(ctx, AR_ERR_UNSUPPORTED,
-                        "TREE, TREE_FUSED and DOUBLE_TREE are AllReduce algorithms; use "
+                        "TREE, TREE_FUSED, DOUBLE_TREE and DOUBLE_TREE_FUSED are AllReduce "
+                        "algorithms; use "
                         "RING_STEP, RING_FUSED, HALVING_DOUBLING or HALVING_DOUBLING_FUSED");
         if (needs_pow2(algo) && !pow2(nranks))
             return fail(ctx, AR_ERR_UNSUPPORTED, "algo %d needs a power-of-two nranks, got %d",
@@ -721,13 +735,14 @@ ar_status ar_auto_algo(int nranks, size_t count, ar_dtype dtype, ar_algo* out) {
 ar_status ar_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* len) {
     if (!offset || !len || nranks < 1 || nranks > AR_MAX_RANKS || chunk < 0 || chunk >= nranks)
         return AR_ERR_INVALID_ARG;
+    // L = ceil(count / N) without forming count + N - 1; lo and hi are
+    // clamped to count without forming chunk * L or lo + L when they would
+    // pass it (both can exceed SIZE_MAX for counts near SIZE_MAX)
     const size_t per = count / (size_t)nranks + (count % (size_t)nranks ? 1 : 0);
-    size_t lo = (size_t)chunk * per;
-    if (lo > count) lo = count;
-    size_t hi = lo + per;
-    if (hi > count) hi = count;
+    const size_t lo = per != 0 && (size_t)chunk > count / per ? count
+                      : std::min((size_t)chunk * per, count);
     *offset = lo;
-    *len = hi - lo;
+    *len = count - lo < per ? count - lo : per;
     return AR_OK;
 }
 
@@ -750,6 +765,44 @@ ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes) {
         return fail(ctx, AR_ERR_RUNTIME, "copy launch failed: %s", hipGetErrorString(e));
     }
     return AR_OK;
+}
+
+ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* dst, int ndst,
+                    size_t bytes) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    try {
+        if (nsrc < 0 || ndst < 0 || nsrc + ndst < 1 || nsrc + ndst > AR_MAX_RANKS)
+            return fail(ctx, AR_ERR_INVALID_ARG, "nsrc %d + ndst %d outside [1, %d]", nsrc, ndst,
+                        AR_MAX_RANKS);
+        if ((nsrc && !src) || (ndst && !dst)) return fail(ctx, AR_ERR_INVALID_ARG, "NULL array");
+        if (bytes % 16) return fail(ctx, AR_ERR_INVALID_ARG, "bytes %zu is not a multiple of 16",
+                                    bytes);
+        if (bytes == 0) return AR_OK;
+        // every buffer: device memory of this device, 16-byte aligned, no overlap
+        std::vector<void*> all;
+        for (int i = 0; i < nsrc; ++i) all.push_back(const_cast<void*>(src[i]));
+        for (int i = 0; i < ndst; ++i) all.push_back(dst[i]);
+        for (size_t i = 0; i < all.size(); ++i)
+            if (reinterpret_cast<uintptr_t>(all[i]) & 15u)
+                return fail(ctx, AR_ERR_INVALID_ARG, "buffer %zu is not 16-byte aligned", i);
+        bool vec;
+        unsigned mis;
+        const ar_status s =
+            check_buffers(ctx, all.data(), (int)all.size(), bytes / 4, AR_INT32, &vec, &mis);
+        if (s != AR_OK) return s;
+        DeviceGuard g(ctx->device);
+        if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
+        const hipError_t e = arlib::launch_stream(src, nsrc, dst, ndst, bytes, ctx->stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ctx, AR_ERR_RUNTIME, "stream launch failed: %s", hipGetErrorString(e));
+        }
+        return AR_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(ctx, AR_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
+    }
 }
 
 const char* ar_status_string(ar_status s) {

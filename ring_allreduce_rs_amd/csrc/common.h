@@ -8,42 +8,17 @@
 
 namespace arlib {
 
-#ifndef AR_FUSED_NT
-#define AR_FUSED_NT 1
-#endif
-#ifndef AR_STEP_NT
-#define AR_STEP_NT 0
-#endif
-
-#ifndef AR_FUSED_THREADS
-#define AR_FUSED_THREADS 64
-#endif
-#ifndef AR_FUSED_UNROLL
-#define AR_FUSED_UNROLL 4
-#endif
-#ifndef AR_SPECIALIZE_N
-#define AR_SPECIALIZE_N 1
-#endif
-
 constexpr int kThreads = 256;       // per-step kernels: 4 wavefronts of 64
 constexpr int kUnroll = 2;          // per-step kernels: 16-byte units per lane per tile
-constexpr int kFusedThreads = AR_FUSED_THREADS;
-constexpr int kFusedUnroll = AR_FUSED_UNROLL;
+constexpr int kFusedThreads = 64;   // fused kernels: one wavefront per block
+constexpr int kFusedUnroll = 4;     // fused WIDE shape: 16-byte units per lane
 constexpr int kBatch = 8;           // ranks of loads issued before they are folded
 // Fused-kernel shapes (units of 16 bytes per lane, ranks of loads in flight
-// before folding).  WIDE suits 8 ranks; with many ranks the fold would wait on
-// memory N/8 times, so DEEP keeps 32 ranks of loads in flight (a 64-rank fold
-// waits twice); MID sits between for 9-16 ranks.  fused_variant() picks one.
-#ifndef AR_FUSED_FORCE_CFG
-#define AR_FUSED_FORCE_CFG -1
-#endif
-#ifndef AR_FUSED_TINY_MAX_CHUNK_BYTES
-#define AR_FUSED_TINY_MAX_CHUNK_BYTES 4096u
-#endif
-#ifndef AR_FUSED_DEEP_MAX_CHUNK_BYTES
-#define AR_FUSED_DEEP_MAX_CHUNK_BYTES (256u << 10)
-#endif
-
+// before folding).  WIDE suits up to 16 ranks; with many ranks the fold would
+// wait on memory N/8 times, so DEEP keeps 32 ranks of loads in flight (a
+// 64-rank fold waits twice).  fused_variant() picks one.
+constexpr size_t kTinyMaxChunkBytes = 4096;        // TINY: chunks up to 4 KiB, > 32 ranks
+constexpr size_t kDeepMaxChunkBytes = 256u << 10;  // 9-16 ranks: DEEP up to 256 KiB chunks
 struct FusedWide {
     static constexpr int U = kFusedUnroll;
     static constexpr int B = kBatch;
@@ -54,11 +29,6 @@ struct FusedDeep {
     static constexpr int B = 32;
     static constexpr bool kWrapLoads = false;
 };
-struct FusedMid {
-    static constexpr int U = 2;
-    static constexpr int B = 16;
-    static constexpr bool kWrapLoads = false;
-};
 // TINY: element-wise units with every rank's load in flight at once (one
 // memory round trip for up to 64 ranks instead of DEEP's two); for chunks so
 // small that latency, not bandwidth, sets the time.
@@ -67,8 +37,7 @@ struct FusedTiny {
     static constexpr int B = AR_MAX_RANKS;
     static constexpr bool kWrapLoads = true;
 };
-enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_MID = 2, CFG_TINY = 3 };
-#define CFG_MID_VALUE 2   // for the preprocessor: MID kernels exist only when forced
+enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_TINY = 2 };
 constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
 constexpr size_t kLeadUnits = 7;    // most idle 16-byte units before a chunk body (128-byte lines)
 // Streaming (non-temporal) loads and stores.  The fused kernel touches every
@@ -77,8 +46,8 @@ constexpr size_t kLeadUnits = 7;    // most idle 16-byte units before a chunk bo
 // kernels are the opposite case: each step re-reads what the previous step
 // wrote, and a 200 MiB working set stays in the 256 MB Infinity Cache when
 // the stores are ordinary (ring 8 x 25 MiB: 169 us with, 189 us without).
-constexpr bool kFusedNT = AR_FUSED_NT != 0;
-constexpr bool kStepNT = AR_STEP_NT != 0;
+constexpr bool kFusedNT = true;
+constexpr bool kStepNT = false;
 constexpr int kCopyUnroll = 1;  // the plain copy streams best with one unit per lane
 
 struct Args {

@@ -1,5 +1,7 @@
-// copy.hip -- plain 16-byte device copy: the reference stream for bandwidth
-// ceilings and for scaling the hardware byte counters.
+// copy.hip -- calibration streams: a plain 16-byte device copy (the reference
+// stream for bandwidth ceilings and for scaling the hardware byte counters),
+// and an R-read / W-write stream laid out like the fused AllReduce kernel
+// (the ceiling of its access pattern without the reduction).
 #include "common.h"
 
 namespace arlib {
@@ -27,6 +29,101 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t str
     if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), nvec);
+    return hipGetLastError();
+}
+
+// R-read / W-write stream.  The tiling is the fused kernel's WIDE shape: one
+// 64-lane wave per block, 4 units of 16 bytes per lane, so block b reads the
+// same 4 KiB of every source and writes the same 4 KiB of every destination;
+// sources are loaded 8 at a time before they are combined, destinations are
+// written one after another.  The sources are combined with XOR (one bitwise
+// instruction per word and source, no rounding), which keeps every load
+// needed and makes the output checkable.  With no source the destinations
+// get zeros; with no destination the combination is kept alive in a
+// register so the loads still happen.  NR > 0 fixes both counts at compile
+// time (the 8-rank fused kernel's fully unrolled form); NR == 0 reads them.
+struct StreamArgs {
+    RankTable src;
+    RankTable dst;
+    size_t units;   // 16-byte units per buffer
+    int nsrc;
+    int ndst;
+};
+
+template <int NR>
+__global__ __launch_bounds__(kFusedThreads) void k_stream(const StreamArgs a) {
+    constexpr int U = FusedWide::U;
+    constexpr int kB = FusedWide::B;
+    constexpr int kMax = NR > 0 ? NR : AR_MAX_RANKS;
+    const int ns = NR > 0 ? NR : a.nsrc;
+    const int nd = NR > 0 ? NR : a.ndst;
+    const size_t ubase = (size_t)blockIdx.x * (kFusedThreads * U) + threadIdx.x;
+    bool ok[U];
+    size_t off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t idx = ubase + (size_t)u * kFusedThreads;
+        ok[u] = idx < a.units;
+        off[u] = idx * 16;
+    }
+    u32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j0 = 0; j0 < kMax; j0 += kB) {
+        if (NR == 0 && j0 >= ns) break;
+        u32x4 v[kB][U];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            if (j0 + j < ns) {
+                const char* s = reinterpret_cast<const char*>(a.src.p[j0 + j]);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[j][u] = ok[u] ? ld16<kFusedNT>(s + off[u]) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            if (j0 + j < ns) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[u] ^= v[j][u];
+            }
+        }
+    }
+    if (nd == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(acc[u]));
+        return;
+    }
+#pragma unroll
+    for (int w = 0; w < kMax; ++w) {
+        if (NR == 0 && w >= nd) break;
+        char* d = reinterpret_cast<char*>(a.dst.p[w]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ok[u]) st16<kFusedNT>(d + off[u], acc[u]);
+    }
+}
+
+hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
+                         size_t bytes, hipStream_t stream) {
+    if (nsrc < 0 || ndst < 0 || nsrc > AR_MAX_RANKS || ndst > AR_MAX_RANKS)
+        return hipErrorInvalidValue;
+    StreamArgs a;
+    for (int r = 0; r < AR_MAX_RANKS; ++r) {
+        a.src.p[r] = r < nsrc ? const_cast<void*>(src[r]) : nullptr;
+        a.dst.p[r] = r < ndst ? dst[r] : nullptr;
+    }
+    a.units = bytes / 16;
+    a.nsrc = nsrc;
+    a.ndst = ndst;
+    if (a.units == 0 || nsrc + ndst == 0) return hipSuccess;
+    const size_t blocks = ceil_div(a.units, (size_t)kFusedThreads * FusedWide::U);
+    if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    if (nsrc == 8 && ndst == 8)
+        hipLaunchKernelGGL(k_stream<8>, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(k_stream<0>, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -6,7 +6,6 @@ namespace arlib {
 
 int fused_variant(const Plan& p) {
     if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return CFG_WIDE;
-    if (AR_FUSED_FORCE_CFG >= 0) return AR_FUSED_FORCE_CFG;
     // Measured on MI355X (fused AllReduce, inputs cold in HBM): WIDE is best
     // for fp32 / int32 at 8 and 16 ranks (8 x 25 MiB: 74 us vs 83 us DEEP;
     // 16 x 1 GiB: 6.9 ms vs 7.7 ms); DEEP for 64 ranks (64 x 64 MiB: 1.60 ms
@@ -17,19 +16,23 @@ int fused_variant(const Plan& p) {
     // (every rank's element load in flight at once: 64 x 4 KiB 8.3 -> 5.0 us,
     // 64 x 64 KiB 8.1 -> 5.5 us); at 16 KiB chunks its 4-byte loads lose
     // (64 x 1 MiB: 23 -> 32 us).
-    const size_t per = ceil_div(p.count, (size_t)p.nranks) * (size_t)elem_bytes(p.dtype);
-    if (p.nranks > FusedDeep::B && per <= (size_t)AR_FUSED_TINY_MAX_CHUNK_BYTES) return CFG_TINY;
+    const size_t per = ceil_div(p.count, (size_t)fused_parts(p.order, p.nranks)) *
+                       (size_t)elem_bytes(p.dtype);
+    // (not the double tree: its 64-position in-order scan does not unroll in
+    // the TINY shape, and the compiler would keep the pending values in
+    // scratch memory; DEEP serves it)
+    if (p.nranks > FusedDeep::B && per <= kTinyMaxChunkBytes && p.order != ORDER_DTREE)
+        return CFG_TINY;
     if (p.dtype == AR_BFLOAT16 || p.nranks > 16) return CFG_DEEP;
-    // the pairwise orders have a WIDE kernel for 8 ranks only (a wider one
-    // would need a deeper stack of subtree results in registers)
-    if (p.order != ORDER_RING) return AR_SPECIALIZE_N && p.nranks == 8 && p.vec ? CFG_WIDE : CFG_DEEP;
+    // the tree orders have a WIDE kernel for 8 ranks only (a wider one would
+    // need a deeper stack of subtree results in registers)
+    if (p.order != ORDER_RING) return p.nranks == 8 && p.vec ? CFG_WIDE : CFG_DEEP;
     if (p.nranks <= kBatch) return CFG_WIDE;
-    return per <= (size_t)AR_FUSED_DEEP_MAX_CHUNK_BYTES ? CFG_DEEP : CFG_WIDE;
+    return per <= kDeepMaxChunkBytes ? CFG_DEEP : CFG_WIDE;
 }
 
 int fused_units_per_lane(int cfg) {
     return cfg == CFG_DEEP   ? FusedDeep::U
-           : cfg == CFG_MID  ? FusedMid::U
            : cfg == CFG_TINY ? FusedTiny::U
                              : FusedWide::U;
 }
@@ -63,10 +66,13 @@ bool plan_shape(const Plan& p, Shape* out) {
         tiles = ceil_div(ceil_div(per * d, epu), per_tile);
         groups = (size_t)p.nranks;
     } else {
-        const size_t per = ceil_div(p.count, (size_t)p.nranks);
+        // ring steps and fused kinds: one group per chunk (fused double tree:
+        // per half)
+        const size_t parts = fused ? (size_t)fused_parts(p.order, p.nranks) : (size_t)p.nranks;
+        const size_t per = ceil_div(p.count, parts);
         const size_t slack = fused && p.lead && epu > 1 ? kLeadUnits : 0;
         tiles = ceil_div(ceil_div(per, epu) + slack, per_tile);
-        groups = (size_t)p.nranks;
+        groups = parts;
     }
     if (tiles == 0) tiles = 1;
     const size_t blocks = tiles * groups;
@@ -80,10 +86,11 @@ bool plan_shape(const Plan& p, Shape* out) {
 hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream) {
     Shape sh;
     if (!plan_shape(p, &sh)) return hipErrorInvalidConfiguration;
+    const bool fused = p.kind == KIND_FUSED_AR || p.kind == KIND_FUSED_RS || p.kind == KIND_FUSED_AG;
     Args a;
     a.t = t;
     a.count = p.count;
-    a.per = ceil_div(p.count, (size_t)p.nranks);
+    a.per = ceil_div(p.count, (size_t)(fused ? fused_parts(p.order, p.nranks) : p.nranks));
     a.n = p.nranks;
     a.step = p.step;
     a.tiles = sh.tiles;
@@ -92,8 +99,6 @@ hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream) {
     a.nf = (float)p.nranks;
     a.inv = (p.nranks & (p.nranks - 1)) == 0 ? 1.0f / (float)p.nranks : 0.0f;
     const dim3 grid(sh.blocks);
-
-    const bool fused = p.kind == KIND_FUSED_AR || p.kind == KIND_FUSED_RS || p.kind == KIND_FUSED_AG;
     return fused ? launch_fused_kind(p, a, grid, stream) : launch_step_kind(p, a, grid, stream);
 }
 

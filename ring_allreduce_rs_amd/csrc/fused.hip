@@ -11,7 +11,7 @@ static hipError_t launch_fused_ag(const Plan& p, const Args& a, dim3 grid, hipSt
     // layout (lead 0 when the layout is aligned).  Measured on MI355X against
     // the run-time-N kernel: 8 x 25 MiB fp32 37.2 vs 38.9 us, bf16 -2 %,
     // ragged counts -1.6 %; the plain 8-rank form was slower (40.1 us).
-    if (AR_SPECIALIZE_N && p.vec && p.nranks == 8) {
+    if (p.vec && p.nranks == 8) {
         hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 8, FusedWide, ORDER_RING, true>),
                            grid, block, 0, s, a);
         return hipGetLastError();

@@ -63,7 +63,7 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
                 if (ok[u]) X::st(dst + off[u], acc[u]);
         }
         return;
-    } else if constexpr (ORDER != ORDER_RING) {
+    } else if constexpr (ORDER == ORDER_PAIR || ORDER == ORDER_PAIR_BITREV) {
         // Pairwise tree over positions 0..n-1 (n a power of two); position q
         // holds rank q (PAIR) or rank bitrev(q) (PAIR_BITREV).  Each batch of
         // bn positions is folded as a subtree; batch results are merged as
@@ -119,6 +119,73 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
                 }
             }
         }
+    } else if constexpr (ORDER == ORDER_DTREE) {
+        // Double binary tree c (0 or 1) over positions 0..n-1 (n a power of
+        // two); position p holds rank (p - c) mod n.  Position 0 is the root,
+        // whose one child is n/2; a position whose lowest set bit is b > 1 has
+        // children p - b/2 and p + b/2, so every subtree spans consecutive
+        // positions.  A node folds (left (+) own) (+) right, the root own (+)
+        // child.  The positions are scanned in order: an odd p is a finished
+        // one-node subtree; as long as the finished subtree is a right child
+        // (bit i of p set at level i) it closes its parent with the pending
+        // (left (+) own) kept in pend[i]; an even p > 0 leaves its own pending
+        // value in pend[ctz p].  With the loops unrolled every position and
+        // level is a compile-time constant; only the rank count bounds them.
+        (void)start;
+        constexpr int kMaxN = NR > 0 ? NR : AR_MAX_RANKS;
+        constexpr int kMaxL = ilog2(kMaxN);
+        const int bn = n < kB ? n : kB;
+        T root[U], cur[U];
+        T pend[kMaxL > 0 ? kMaxL : 1][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) root[u] = cur[u] = X::zero();
+#pragma unroll
+        for (int j0 = 0; j0 < kMaxN; j0 += kB) {
+            if (NR == 0 && j0 >= n) break;
+            T v[kB][U];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                if (CFG::kWrapLoads || j < bn) {
+                    const int q = j0 + (j & (bn - 1));
+                    const int rank = q >= c ? q - c : q - c + n;
+                    const char* src = rank_ptr(a, rank);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[j][u] = ok[u] ? X::ld(src + off[u]) : X::zero();
+                }
+            }
+            if constexpr (CFG::kWrapLoads) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                // (no early exits: they keep the compiler from unrolling these
+                // loops, and the pending values would go to scratch memory)
+                if (j >= bn) continue;
+                const int p = j0 + j;
+                if (p == 0) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) root[u] = v[j][u];
+                } else if (p & 1) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) cur[u] = v[j][u];
+                    // climb while the finished subtree is a right child: level
+                    // i is reached when bits 1..i of p are all set
+#pragma unroll
+                    for (int i = 1; i < kMaxL; ++i) {
+                        const int m = (2 << i) - 2;
+                        if ((p & m) == m) {
+#pragma unroll
+                            for (int u = 0; u < U; ++u) cur[u] = X::comb(pend[i][u], cur[u]);
+                        }
+                    }
+                } else {
+                    const int lvl = __builtin_ctz((unsigned)p);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) pend[lvl][u] = X::comb(cur[u], v[j][u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = n > 1 ? X::comb(root[u], cur[u]) : root[u];
     }
     if constexpr (MODE != KIND_FUSED_AG) {
         if constexpr (ORDER == ORDER_RING) {
@@ -235,7 +302,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
 // WIDE shapes, and 3.7 % slower on the 8-rank WIDE kernel, which therefore
 // keeps the plain indexing when the layout allows it.
 inline bool use_lead(const Plan& p) {
-    const bool n8_wide = AR_SPECIALIZE_N && p.nranks == 8 && fused_variant(p) == CFG_WIDE;
+    const bool n8_wide = p.nranks == 8 && fused_variant(p) == CFG_WIDE;
     return p.vec && (p.lead || !n8_wide);
 }
 
@@ -243,21 +310,21 @@ template <class Op, int MODE, bool VEC, int ORDER, bool LEAD = false>
 inline hipError_t launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
     const dim3 block(kFusedThreads);
     const int cfg = fused_variant(p);
-    const bool n8 = AR_SPECIALIZE_N && VEC && p.nranks == 8;
+    const bool n8 = VEC && p.nranks == 8;
     if constexpr (VEC && !LEAD) {
         // plain 16-byte indexing: the aligned 8-rank WIDE kernel only (use_lead)
         if (!n8 || cfg != CFG_WIDE) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedWide, ORDER>), grid, block, 0, s, a);
     } else if (cfg == CFG_TINY) {
-        // element-wise units whatever the alignment (the grid was sized so)
-        hipLaunchKernelGGL((k_fused<Op, MODE, false, 0, FusedTiny, ORDER>), grid, block, 0, s, a);
+        // element-wise units whatever the alignment (the grid was sized so);
+        // never planned for the double tree (fused_variant)
+        if constexpr (ORDER == ORDER_DTREE) return hipErrorInvalidConfiguration;
+        else
+            hipLaunchKernelGGL((k_fused<Op, MODE, false, 0, FusedTiny, ORDER>), grid, block, 0, s,
+                               a);
     } else if (cfg == CFG_DEEP) {
         // the runtime-N loop measured faster than the 8-rank unrolled one here
         hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep, ORDER, LEAD>), grid, block, 0, s, a);
-#if AR_FUSED_FORCE_CFG == CFG_MID_VALUE
-    } else if (cfg == CFG_MID) {
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedMid, ORDER, LEAD>), grid, block, 0, s, a);
-#endif
     } else if (n8) {
         hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide, ORDER, LEAD>), grid, block, 0, s, a);
     } else if constexpr (ORDER == ORDER_RING) {
@@ -294,6 +361,9 @@ inline hipError_t launch_fused_op(const Plan& p, const Args& a, dim3 grid, hipSt
         case ORDER_PAIR_BITREV:
             e = rs ? launch_fused_v<Op, KIND_FUSED_RS, ORDER_PAIR_BITREV, LEAD>(p, a, grid, s)
                    : launch_fused_v<Op, KIND_FUSED_AR, ORDER_PAIR_BITREV, LEAD>(p, a, grid, s);
+            break;
+        case ORDER_DTREE:   // double binary tree: AllReduce only
+            if (!rs) e = launch_fused_v<Op, KIND_FUSED_AR, ORDER_DTREE, LEAD>(p, a, grid, s);
             break;
         default:
             break;

@@ -32,9 +32,15 @@ enum Kind {
 // c+1, ..., c (the ring's order).  PAIR: a pairwise tree over ranks 0..N-1 in
 // index order (recursive doubling's result).  PAIR_BITREV: the same tree over
 // ranks in bit-reversed order, i.e. partners at distance N/2 first
-// (recursive halving-doubling's result).  The pairwise orders need a
-// power-of-two N.
-enum Order { ORDER_RING = 0, ORDER_PAIR = 1, ORDER_PAIR_BITREV = 2 };
+// (recursive halving-doubling's result).  DTREE: the double binary tree's
+// in-order folds, the first ceil(count/2) elements over tree 0 and the rest
+// over tree 1 (the double tree's result); its "chunks" are those two halves.
+// The tree orders need a power-of-two N.
+enum Order { ORDER_RING = 0, ORDER_PAIR = 1, ORDER_PAIR_BITREV = 2, ORDER_DTREE = 3 };
+
+// Parts the fused kernels split a rank's vector into: N chunks, or the double
+// tree's two halves.
+inline int fused_parts(int order, int nranks) { return order == ORDER_DTREE ? 2 : nranks; }
 
 struct Plan {
     Kind kind;
@@ -66,5 +72,10 @@ hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream);
 
 // 16-byte vector copy of `bytes` (multiple of 16, both pointers 16-byte aligned).
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+// Calibration stream: read `bytes` from each of nsrc buffers, write their XOR
+// to each of ndst buffers (16-byte aligned pointers, bytes a multiple of 16).
+hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
+                         size_t bytes, hipStream_t stream);
 
 }  // namespace arlib

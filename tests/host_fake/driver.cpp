@@ -74,7 +74,7 @@ void check_chunk_range() {
 void check_cost_model() {
     const ar_algo algos[] = {AR_ALGO_RING_STEP, AR_ALGO_RING_FUSED, AR_ALGO_TREE,
                              AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE, AR_ALGO_TREE_FUSED,
-                             AR_ALGO_HALVING_DOUBLING_FUSED};
+                             AR_ALGO_HALVING_DOUBLING_FUSED, AR_ALGO_DOUBLE_TREE_FUSED};
     const ar_dtype dts[] = {AR_INT32, AR_FLOAT32, AR_BFLOAT16};
     for (int n = 1; n <= kMaxN; ++n)
         for (ar_dtype dt : dts)
@@ -87,7 +87,8 @@ void check_cost_model() {
                     const ar_status st = ar_predict_us(a, n, count, dt, &us);
                     const bool needs_pow2 = a == AR_ALGO_TREE || a == AR_ALGO_HALVING_DOUBLING ||
                                             a == AR_ALGO_DOUBLE_TREE || a == AR_ALGO_TREE_FUSED ||
-                                            a == AR_ALGO_HALVING_DOUBLING_FUSED;
+                                            a == AR_ALGO_HALVING_DOUBLING_FUSED ||
+                                            a == AR_ALGO_DOUBLE_TREE_FUSED;
                     if (needs_pow2 && !pow2(n)) {
                         CHECK(st == AR_ERR_UNSUPPORTED, "predict needs pow2");
                         continue;
@@ -190,6 +191,7 @@ struct Expect {
 
 int order_of(int coll, ar_algo algo) {
     if (algo == AR_ALGO_TREE_FUSED) return arlib::ORDER_PAIR;
+    if (algo == AR_ALGO_DOUBLE_TREE_FUSED) return arlib::ORDER_DTREE;
     if (algo == AR_ALGO_HALVING_DOUBLING_FUSED && coll != 2) return arlib::ORDER_PAIR_BITREV;
     return arlib::ORDER_RING;
 }
@@ -202,6 +204,7 @@ std::vector<Expect> expected(int coll, ar_algo algo, int n) {
         case AR_ALGO_RING_FUSED:
         case AR_ALGO_TREE_FUSED:
         case AR_ALGO_HALVING_DOUBLING_FUSED:
+        case AR_ALGO_DOUBLE_TREE_FUSED:
             e.push_back({coll == 0 ? arlib::KIND_FUSED_AR
                                    : coll == 1 ? arlib::KIND_FUSED_RS : arlib::KIND_FUSED_AG, 0});
             break;
@@ -255,7 +258,8 @@ void check_launches(ar_ctx* ctx) {
     std::mt19937_64 rng(12345);
     const ar_algo algos[] = {AR_ALGO_RING_STEP, AR_ALGO_RING_FUSED, AR_ALGO_TREE,
                              AR_ALGO_HALVING_DOUBLING, AR_ALGO_DOUBLE_TREE, AR_ALGO_AUTO,
-                             AR_ALGO_TREE_FUSED, AR_ALGO_HALVING_DOUBLING_FUSED};
+                             AR_ALGO_TREE_FUSED, AR_ALGO_HALVING_DOUBLING_FUSED,
+                             AR_ALGO_DOUBLE_TREE_FUSED};
     const ar_dtype dts[] = {AR_INT32, AR_FLOAT32, AR_BFLOAT16};
     const ar_op ops[] = {AR_SUM, AR_MAX, AR_AVG};
     const size_t special[] = {1, 2, 3, 7, 15, 16, 17, 63, 64, 65, 4095, 4096, 4097, 65536,
@@ -281,7 +285,7 @@ void check_launches(ar_ctx* ctx) {
         fake_clear_executed();
         const ar_status st = call(ctx, coll, bufs, n, count, dt, op, algo);
         const bool tree_only = algo == AR_ALGO_TREE || algo == AR_ALGO_DOUBLE_TREE ||
-                               algo == AR_ALGO_TREE_FUSED;
+                               algo == AR_ALGO_TREE_FUSED || algo == AR_ALGO_DOUBLE_TREE_FUSED;
         const bool needs_pow2 = tree_only || algo == AR_ALGO_HALVING_DOUBLING ||
                                 algo == AR_ALGO_HALVING_DOUBLING_FUSED;
         char what[160];
@@ -298,7 +302,9 @@ void check_launches(ar_ctx* ctx) {
         ar_algo resolved = algo;
         if (algo == AR_ALGO_AUTO) {
             (void)ar_auto_algo(n, count, dt, &resolved);
-            if ((resolved == AR_ALGO_TREE || resolved == AR_ALGO_DOUBLE_TREE) && coll != 0)
+            if ((resolved == AR_ALGO_TREE || resolved == AR_ALGO_DOUBLE_TREE ||
+                 resolved == AR_ALGO_TREE_FUSED || resolved == AR_ALGO_DOUBLE_TREE_FUSED) &&
+                coll != 0)
                 resolved = AR_ALGO_RING_FUSED;
         }
         // a call whose kernels do not all fit one grid is refused before any launch
@@ -315,7 +321,8 @@ void check_launches(ar_ctx* ctx) {
                 p.vec = !mixed;
                 p.mis = mixed ? 0u : (unsigned)shift;
                 p.order = order_of(coll, resolved);
-                const size_t cb = (count + (size_t)n - 1) / (size_t)n * eb;
+                const size_t parts = resolved == AR_ALGO_DOUBLE_TREE_FUSED ? 2 : (size_t)n;
+                const size_t cb = (count + parts - 1) / parts * eb;
                 const bool fused_kind = e.kind == arlib::KIND_FUSED_AR ||
                                         e.kind == arlib::KIND_FUSED_RS || e.kind == arlib::KIND_FUSED_AG;
                 p.lead = fused_kind && p.vec &&
@@ -337,8 +344,9 @@ void check_launches(ar_ctx* ctx) {
             continue;
         }
         check_sequence(fake_executed(), coll, resolved, n, count, dt, op, bufs, what);
+        const size_t parts = resolved == AR_ALGO_DOUBLE_TREE_FUSED ? 2 : (size_t)n;
         const bool lines = (reinterpret_cast<uintptr_t>(bufs[0]) & 127u) == 0 &&
-                           (count + (size_t)n - 1) / (size_t)n * eb % 128 == 0;
+                           (count + parts - 1) / parts * eb % 128 == 0;
         for (const FakeLaunch& l : fake_executed()) {
             CHECK(l.plan.order == order_of(coll, resolved), "%s: fold order %d", what, l.plan.order);
             const bool vec = !mixed;

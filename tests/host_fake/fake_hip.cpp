@@ -96,8 +96,13 @@ void expected_work(const arlib::Plan& p, const arlib::Args& a, size_t* elems, si
             *groups = n;
             break;
         default:
-            *elems = per;
-            *groups = n;
+            if (p.order == arlib::ORDER_DTREE) {   // fused double tree: two halves
+                *elems = (p.count + 1) / 2;
+                *groups = 2;
+            } else {
+                *elems = per;
+                *groups = n;
+            }
             break;
     }
     (void)a;
@@ -138,7 +143,8 @@ void record(const arlib::Plan& p, const arlib::Args& a, dim3 grid, hipStream_t s
         coverage_fail("tiles do not cover the group's elements", a, grid);
     else if (elems > 0 && ((size_t)a.tiles - 1) * threads * upl * epu >= elems + lead + threads * upl * epu)
         coverage_fail("more tiles than the work needs", a, grid);
-    if (a.n != p.nranks || a.count != p.count || a.per != (p.count + p.nranks - 1) / p.nranks)
+    const size_t parts = fused ? (size_t)arlib::fused_parts(p.order, p.nranks) : (size_t)p.nranks;
+    if (a.n != p.nranks || a.count != p.count || a.per != (p.count + parts - 1) / parts)
         coverage_fail("kernel arguments disagree with the plan", a, grid);
     for (int r = 0; r < p.nranks; ++r)
         if (!a.t.p[r]) coverage_fail("NULL rank pointer passed to a kernel", a, grid);
@@ -174,6 +180,10 @@ hipError_t launch_step_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t
     return hipSuccess;
 }
 hipError_t launch_copy(void*, const void*, size_t, hipStream_t) {
+    ++g_count.kernel_launches;
+    return hipSuccess;
+}
+hipError_t launch_stream(const void* const*, int, void* const*, int, size_t, hipStream_t) {
     ++g_count.kernel_launches;
     return hipSuccess;
 }

@@ -57,6 +57,21 @@ def test_chunk_range_matches_oracle_layout(n):
             assert ar.chunk_range(count, n, c) == lay[c]
 
 
+@pytest.mark.parametrize("n", [2, 3, 63, 64])
+def test_chunk_range_near_size_max(n):
+    """Counts near 2^64 - 1: the ceiling split must hold exactly (no wrap in
+    c*L or lo + L); the oracle's layout uses Python integers."""
+    import ring_allreduce_rs_amd as ar
+    top = (1 << 64) - 1
+    for count in (top, top - 1, top - n, (1 << 63) + 1):
+        lay = oracle.chunk_layout(count, n)
+        got = [ar.chunk_range(count, n, c) for c in range(n)]
+        assert got == lay
+        assert sum(ln for _, ln in got) == count
+    # the case that once wrapped: 2 ranks, chunk 1 of 2^64 - 1 elements
+    assert ar.chunk_range(top, 2, 1) == (1 << 63, (1 << 63) - 1)
+
+
 def test_chunk_range_rejects_bad_arguments():
     import ring_allreduce_rs_amd as ar
     for count, n, c in ((10, 0, 0), (10, 65, 0), (10, 4, 4), (10, 4, -1)):

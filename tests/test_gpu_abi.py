@@ -155,3 +155,44 @@ def test_stream_binding_orders_work():
     s.synchronize()
     for t in ts:
         assert (t.cpu() == 28.0).all()
+
+
+@pytest.mark.parametrize("nsrc,ndst", [(1, 1), (8, 8), (3, 5), (16, 16), (0, 2), (4, 0), (1, 8)])
+def test_calibration_stream_writes_the_xor(nsrc, ndst):
+    """ar_stream: every destination receives the XOR of the sources (zeros
+    with no source); the sources are left unchanged; sizes span several 4 KiB
+    tiles and a partial last tile."""
+    nbytes = 3 * 4096 + 48
+    g = torch.Generator(device="cpu").manual_seed(nsrc * 100 + ndst)
+    srcs = [torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32).cuda()
+            for _ in range(nsrc)]
+    keep = [s.clone() for s in srcs]
+    dsts = [torch.full((nbytes // 4,), -1, dtype=torch.int32, device="cuda") for _ in range(ndst)]
+    ar.stream_(srcs, dsts)
+    torch.cuda.synchronize()
+    want = np.zeros(nbytes // 4, np.int32)
+    for s in keep:
+        want ^= s.cpu().numpy()
+    for d in dsts:
+        assert np.array_equal(d.cpu().numpy(), want)
+    for s, k in zip(srcs, keep):
+        assert torch.equal(s, k)
+
+
+def test_calibration_stream_rejects_bad_arguments(ctx):
+    a = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    b = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    pa, pb = a.data_ptr(), b.data_ptr()
+    cases = {
+        "nothing": lambda: ctx.stream_ptrs([], [], 4096),
+        "65 buffers": lambda: ctx.stream_ptrs([pa] * 33, [pb] * 32, 16),
+        "bytes not a multiple of 16": lambda: ctx.stream_ptrs([pa], [pb], 4000 + 8),
+        "misaligned": lambda: ctx.stream_ptrs([pa + 4], [pb], 1024),
+        "overlap": lambda: ctx.stream_ptrs([pa], [pa + 16], 1024),
+        "past allocation": lambda: ctx.stream_ptrs([pa], [pb], 8192),
+        "host pointer": lambda: ctx.stream_ptrs([np.zeros(256, np.int32).ctypes.data], [pb],
+                                                1024),
+    }
+    for what, fn in cases.items():
+        assert status_of(fn) == INVALID, what
+    ctx.stream_ptrs([pa], [pb], 0)          # zero bytes: a no-op

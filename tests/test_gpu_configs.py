@@ -92,10 +92,11 @@ def test_ddp_bucket_config_full_oracle():
         assert ranks_identical(ts)
         assert_bits_equal(to_np(ts[0]), want, algo)
     dw = oracle.simulate_double_tree_allreduce(xs, "float32", "avg").state[0]
-    ts = to_gpu(xs, "float32")
-    run(ts, "avg", "double_tree")
-    assert ranks_identical(ts)
-    assert_bits_equal(to_np(ts[0]), dw, "double_tree")
+    for algo in ("double_tree", "double_tree_fused"):
+        ts = to_gpu(xs, "float32")
+        run(ts, "avg", algo)
+        assert ranks_identical(ts)
+        assert_bits_equal(to_np(ts[0]), dw, algo)
 
 
 @pytest.mark.slow
@@ -139,7 +140,7 @@ def test_sweep_config(w):
         idx = sample_positions(w.count, w.nranks, k=4096, seed=2)
         vals = gather(a, idx)
     b, c, h, d = clone_all(a), clone_all(a), clone_all(a), clone_all(a)
-    cf, hf = clone_all(a), clone_all(a)
+    cf, hf, df = clone_all(a), clone_all(a), clone_all(a)
     run(a, "sum", "ring_step")
     run(b, "sum", "ring_fused")
     run(c, "sum", "tree")
@@ -147,12 +148,14 @@ def test_sweep_config(w):
     run(d, "sum", "double_tree")
     run(cf, "sum", "tree_fused")
     run(hf, "sum", "halving_doubling_fused")
+    run(df, "sum", "double_tree_fused")
     assert ranks_identical(d)
     for r in range(w.nranks):
         assert torch.equal(a[r], b[r]), f"fused != step on rank {r}"
         assert torch.equal(c[r], cf[r]), f"tree_fused != tree on rank {r}"
         assert torch.equal(h[r], hf[r]), f"halving_doubling_fused != halving_doubling on rank {r}"
-    del cf, hf
+        assert torch.equal(d[r], df[r]), f"double_tree_fused != double_tree on rank {r}"
+    del cf, hf, df
     assert ranks_identical(a) and ranks_identical(c) and ranks_identical(h)
     if full:
         assert_bits_equal(to_np(a[0]), oracle.simulate_ring_allreduce(xs, "float32", "sum").state[0],

@@ -12,6 +12,9 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 RING = ("ring_step", "ring_fused")
+# the tree algorithms, per step and in one pass (power-of-two rank counts)
+TREES = ("tree", "halving_doubling", "double_tree", "tree_fused", "halving_doubling_fused",
+         "double_tree_fused")
 
 
 def h(s):
@@ -30,7 +33,7 @@ def test_three_rank_example(golden, count, algo):
         assert (t.cpu() == g["expected_value_every_rank"]).all()
 
 
-@pytest.mark.parametrize("algo", RING + ("tree", "halving_doubling", "double_tree"))
+@pytest.mark.parametrize("algo", RING + TREES)
 def test_four_rank_example(golden, algo):
     g = golden("four_rank_ones_2x3.json")
     for op, key in (("sum", "expected_sum_every_element"), ("avg", "expected_avg_every_element")):
@@ -42,9 +45,9 @@ def test_four_rank_example(golden, algo):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16, 64])
-@pytest.mark.parametrize("algo", RING + ("tree", "halving_doubling", "double_tree"))
+@pytest.mark.parametrize("algo", RING + TREES)
 def test_rank_valued_closed_form(n, algo):
-    if algo in ("tree", "halving_doubling", "double_tree") and n & (n - 1):
+    if algo in TREES and n & (n - 1):
         pytest.skip("tree needs a power of two")
     for op, want in (("sum", n * (n - 1) / 2), ("avg", (n - 1) / 2)):
         ts = [torch.ones(4, device="cuda") * r for r in range(n)]
@@ -66,15 +69,16 @@ def test_ring_fold_order_golden(golden, algo):
         assert_bits_equal(to_np(t), want, f"{algo} rank {r}")
 
 
-def test_tree_order_golden(golden):
+@pytest.mark.parametrize("algo", ["tree", "tree_fused"])
+def test_tree_order_golden(golden, algo):
     g = golden("tree_order_n4_fp32.json")
     xs = [np.array(x, dtype=np.float32) for x in g["inputs"]]
     ts = to_gpu(xs, "float32")
-    ar.allreduce(ts, op="sum", algo="tree")
+    ar.allreduce(ts, op="sum", algo=algo)
     torch.cuda.synchronize()
     want = np.array(g["expected_every_rank"], dtype=np.float32)
     for r, t in enumerate(ts):
-        assert_bits_equal(to_np(t), want, f"tree rank {r}")
+        assert_bits_equal(to_np(t), want, f"{algo} rank {r}")
 
 
 def _pair_cases(cases, key_a="a", key_b="b"):
@@ -83,7 +87,7 @@ def _pair_cases(cases, key_a="a", key_b="b"):
     return a, b, [h(c["expect"]) for c in cases]
 
 
-@pytest.mark.parametrize("algo", RING + ("tree", "halving_doubling", "double_tree"))
+@pytest.mark.parametrize("algo", RING + TREES)
 @pytest.mark.parametrize("width", [1, 37])
 def test_bf16_bits_golden(golden, algo, width):
     """Two ranks: the one hop is exactly the golden case.  ``width`` repeats the
@@ -104,7 +108,7 @@ def test_bf16_bits_golden(golden, algo, width):
         s = np.array([h(c["sum"])], np.uint16)
         zero = np.zeros(1, np.uint16)
         xs = [s] + [zero] * (n - 1)
-        if algo in ("tree", "halving_doubling", "double_tree") and n & (n - 1):
+        if algo in TREES and n & (n - 1):
             continue
         ts = to_gpu([np.repeat(x, width) for x in xs], "bfloat16")
         ar.allreduce(ts, op="avg", algo=algo)
@@ -113,7 +117,7 @@ def test_bf16_bits_golden(golden, algo, width):
             assert_bits_equal(to_np(t), np.full(width, h(c["expect"]), np.uint16), c["why"])
 
 
-@pytest.mark.parametrize("algo", RING + ("tree", "halving_doubling", "double_tree"))
+@pytest.mark.parametrize("algo", RING + TREES)
 @pytest.mark.parametrize("width", [1, 37])
 def test_fp32_bits_golden(golden, algo, width):
     g = golden("fp32_edge_bits.json")
@@ -129,7 +133,7 @@ def test_fp32_bits_golden(golden, algo, width):
                               f"fp32 {op} {algo}")
     for c in g["cases_avg"]:
         n = c["nranks"]
-        if algo in ("tree", "halving_doubling", "double_tree") and n & (n - 1):
+        if algo in TREES and n & (n - 1):
             continue
         s = np.full(width, h(c["sum"]), np.uint32).view(np.float32)
         xs = [s] + [np.zeros(width, np.float32)] * (n - 1)
@@ -141,7 +145,7 @@ def test_fp32_bits_golden(golden, algo, width):
                               c["why"])
 
 
-@pytest.mark.parametrize("algo", RING + ("tree", "halving_doubling", "double_tree"))
+@pytest.mark.parametrize("algo", RING + TREES)
 def test_int32_wraps(algo):
     xs = [np.array([2**31 - 1, -2**31] * 9, np.int32), np.array([1, -1] * 9, np.int32)]
     ts = to_gpu(xs, "int32")
@@ -151,23 +155,25 @@ def test_int32_wraps(algo):
         assert to_np(t).tolist() == [-2**31, 2**31 - 1] * 9
 
 
-def test_hd_order_golden(golden):
+@pytest.mark.parametrize("algo", ["halving_doubling", "halving_doubling_fused"])
+def test_hd_order_golden(golden, algo):
     g = golden("hd_order_n4_fp32.json")
     xs = [np.array(x, dtype=np.float32) for x in g["inputs"]]
     ts = to_gpu(xs, "float32")
-    ar.allreduce(ts, op="sum", algo="halving_doubling")
+    ar.allreduce(ts, op="sum", algo=algo)
     torch.cuda.synchronize()
     want = np.array(g["expected_every_rank"], dtype=np.float32)
     for r, t in enumerate(ts):
-        assert_bits_equal(to_np(t), want, f"hd rank {r}")
+        assert_bits_equal(to_np(t), want, f"{algo} rank {r}")
 
 
-def test_dtree_order_golden(golden):
+@pytest.mark.parametrize("algo", ["double_tree", "double_tree_fused"])
+def test_dtree_order_golden(golden, algo):
     g = golden("dtree_order_n4_fp32.json")
     xs = [np.array(x, dtype=np.float32) for x in g["inputs"]]
     ts = to_gpu(xs, "float32")
-    ar.allreduce(ts, op="sum", algo="double_tree")
+    ar.allreduce(ts, op="sum", algo=algo)
     torch.cuda.synchronize()
     want = np.array(g["expected_every_rank"], dtype=np.float32)
     for r, t in enumerate(ts):
-        assert_bits_equal(to_np(t), want, f"dtree rank {r}")
+        assert_bits_equal(to_np(t), want, f"{algo} rank {r}")

@@ -184,8 +184,9 @@ def test_unaligned_buffers(dtype, op, shift, same_alignment):
              "halving_doubling": oracle.simulate_hd_allreduce(xs, dtype, op).state,
              "double_tree": oracle.simulate_double_tree_allreduce(xs, dtype, op).state}
     stride = ((count + 64 + 7) // 8) * 8          # a multiple of 16 bytes per row
-    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling", "double_tree"):
-        want = wants["ring" if algo.startswith("ring") else algo]
+    for algo in ("ring_step", "ring_fused", "tree", "halving_doubling", "double_tree",
+                 "tree_fused", "halving_doubling_fused", "double_tree_fused"):
+        want = wants["ring" if algo.startswith("ring") else algo.replace("_fused", "")]
         store = torch.zeros(n * stride, dtype=to_gpu(xs[:1], dtype)[0].dtype, device="cuda")
         views = []
         for r in range(n):
@@ -228,7 +229,10 @@ def test_auto_runs_the_model_choice(dtype, op, n, count):
     sim = {"ring_fused": oracle.simulate_ring_allreduce, "ring_step": oracle.simulate_ring_allreduce,
            "tree": oracle.simulate_tree_allreduce,
            "halving_doubling": oracle.simulate_hd_allreduce,
-           "double_tree": oracle.simulate_double_tree_allreduce}[pick]
+           "double_tree": oracle.simulate_double_tree_allreduce,
+           "tree_fused": oracle.simulate_tree_allreduce,
+           "halving_doubling_fused": oracle.simulate_hd_allreduce,
+           "double_tree_fused": oracle.simulate_double_tree_allreduce}[pick]
     want = sim(xs, dtype, op).state
     ts = to_gpu(xs, dtype)
     ar.allreduce(ts, op=op, algo="auto")
@@ -239,7 +243,7 @@ def test_auto_runs_the_model_choice(dtype, op, n, count):
     ar.reduce_scatter(rs, op=op, algo="auto")
     ar.allgather(rs, algo="auto")
     torch.cuda.synchronize()
-    if pick not in ("tree", "double_tree"):
+    if pick not in ("tree", "double_tree", "tree_fused", "double_tree_fused"):
         for r in range(n):
             assert_bits_equal(to_np(rs[r]), want[r], f"auto RS+AG rank {r}")
 
@@ -303,7 +307,8 @@ def test_fused_many_ranks_small_chunks(dtype, op, n, count):
 POW2 = [(2, 1), (2, 4099), (4, 6), (4, 24581), (8, 1), (8, 1000), (8, 65539), (16, 33),
         (16, 40003), (32, 2050), (64, 63), (64, 4101), (64, 70_001)]
 FUSED_TREES = [("tree_fused", oracle.simulate_tree_allreduce),
-               ("halving_doubling_fused", oracle.simulate_hd_allreduce)]
+               ("halving_doubling_fused", oracle.simulate_hd_allreduce),
+               ("double_tree_fused", oracle.simulate_double_tree_allreduce)]
 
 
 @pytest.mark.parametrize("algo,sim", FUSED_TREES, ids=[a for a, _ in FUSED_TREES])
@@ -338,12 +343,15 @@ def test_fused_halving_doubling_reduce_scatter_then_allgather(dtype, op, n, coun
 
 def test_fused_tree_orders_refuse_what_they_do_not_define():
     ts = to_gpu(rand_inputs("float32", 6, 100, seed=1), "float32")
-    for algo in ("tree_fused", "halving_doubling_fused"):
+    for algo in ("tree_fused", "halving_doubling_fused", "double_tree_fused"):
         with pytest.raises(ar.ArError):
             ar.allreduce(ts, op="sum", algo=algo)           # 6 ranks: not a power of two
     ts = to_gpu(rand_inputs("float32", 8, 100, seed=1), "float32")
-    with pytest.raises(ar.ArError):
-        ar.reduce_scatter(ts, op="sum", algo="tree_fused")  # AllReduce only
+    for algo in ("tree_fused", "double_tree_fused"):
+        with pytest.raises(ar.ArError):
+            ar.reduce_scatter(ts, op="sum", algo=algo)      # AllReduce only
+        with pytest.raises(ar.ArError):
+            ar.allgather(ts, algo=algo)
 
 
 # Chunk bodies that start off a 128-byte line take the line-aligned kernels
@@ -369,7 +377,9 @@ def test_line_aligned_tiles_match_oracle(dtype, op, n, count, line_shift):
     algos = [("ring_fused", want_ring)]
     if n & (n - 1) == 0:
         algos += [("tree_fused", oracle.simulate_tree_allreduce(xs, dtype, op).state),
-                  ("halving_doubling_fused", oracle.simulate_hd_allreduce(xs, dtype, op).state)]
+                  ("halving_doubling_fused", oracle.simulate_hd_allreduce(xs, dtype, op).state),
+                  ("double_tree_fused",
+                   oracle.simulate_double_tree_allreduce(xs, dtype, op).state)]
     for algo, want in algos + [("rs+ag", want_ring)]:
         store = torch.zeros(n * stride + 64, dtype=tdt, device="cuda")
         assert store.data_ptr() % 128 == 0
