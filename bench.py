@@ -16,12 +16,19 @@ Printed (one JSON line):
              synchronisations
   roofline   the dominant kernel's GB/s from HIP events recorded on its stream
              at both ends of the timed region (mean per launch), against the
-             8 TB/s HBM peak; `traffic` is the
-             HBM bytes per launch measured with rocprofv3 counters (scaled by a
-             plain copy of known size) when the kernel source is unchanged
-             since they were taken, else null
-  cpu_baseline  the CPU oracle (message-passing ring simulation, numpy, one
-             core) on the same workload, rank 0 only
+             8 TB/s HBM peak; the median and minimum of per-launch event times
+             from a second pass over the same buckets beside it; `traffic` is
+             the HBM bytes per launch measured with rocprofv3 counters (scaled
+             by a plain copy of known size) when the kernel source is
+             unchanged since they were taken, else null
+  others     the other algorithms on the same buckets, the fused ReduceScatter
+             and AllGather alone, the plain copy and the R-read / W-write
+             calibration streams (ar_stream) over the same bytes per buffer
+  cpu_baseline  the CPU oracle (message-passing simulation, numpy, one core)
+             on the whole workload when it fits the host comfortably, else on
+             the workload's first elements of every rank (the sample is
+             named); the GPU result is checked against the oracle bitwise,
+             whole or at sampled positions
 """
 
 from __future__ import annotations
@@ -79,7 +86,8 @@ def parse():
     ap.add_argument("--workload", default=W.DDP_BUCKET.name, choices=sorted(names))
     ap.add_argument("--algo", default="ring_fused",
                     choices=["ring_fused", "ring_step", "tree", "halving_doubling",
-                             "double_tree", "tree_fused", "halving_doubling_fused"])
+                             "double_tree", "tree_fused", "halving_doubling_fused",
+                             "double_tree_fused"])
     ap.add_argument("--sets", type=int, default=0,
                     help="bucket sets to rotate over (0: enough to exceed the Infinity Cache 4x)")
     ap.add_argument("--seed", type=int, default=0)
@@ -92,6 +100,11 @@ def parse():
                     help="time every algorithm over the 64-rank message-size sweep, fit the "
                          "latency/bandwidth model T = a + b*K per algorithm and report the "
                          "ring/tree crossover (one JSON line per point, then one fit line)")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="time the fused AllReduce, the in-place N-read / N-write calibration "
+                         "stream and the plain copy over the same bytes, for the workload's rank "
+                         "count and dtype at sizes per rank from 0.78 to 400 MiB, and fit "
+                         "T = a + bytes / BW to each (one JSON line per size, then one fit line)")
     a = ap.parse_args()
     return a, names[a.workload]
 
@@ -145,6 +158,70 @@ def copy_ceiling(ar, nbytes, reps=50):
     return 2 * nb / (ms * 1e-3) / 1e9, ms
 
 
+def launch_stats(ar, sets, w, algo, reps):
+    """Per-launch HIP-event times (ms) of `reps` launches rotating over the
+    bucket sets, each launch bracketed by its own pair of events on the launch
+    stream: (median, min, mean)."""
+    import statistics
+
+    import torch
+    calls = [ar.bind(ts, op=w.op, algo=algo) for ts in sets]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        calls[i % len(calls)]()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return statistics.median(ms), min(ms), sum(ms) / len(ms)
+
+
+def stream_ceiling(ar, nsrc, ndst, nbytes, reps=40, in_place=False):
+    """GB/s of the calibration stream reading nsrc and writing ndst buffers of
+    nbytes each (ar_stream: the fused kernel's tiling, no reduction), rotating
+    over buffer sets that together exceed the Infinity Cache 4x.  in_place:
+    the destinations are the sources themselves, as in an AllReduce."""
+    import torch
+    nb = (nbytes // 16) * 16
+    per_set = (nsrc + ndst) * nb
+    nsets = max(1, min(8, -(-4 * INFINITY_CACHE_BYTES // (nsrc if in_place else nsrc + ndst)
+                            // nb)))
+    sets = []
+    for _ in range(nsets):
+        srcs = [torch.ones(nb // 4, dtype=torch.int32, device="cuda") for _ in range(nsrc)]
+        dsts = (srcs[:ndst] if in_place else
+                [torch.empty(nb // 4, dtype=torch.int32, device="cuda") for _ in range(ndst)])
+        sets.append((srcs, dsts))
+    for srcs, dsts in sets:
+        ar.stream_(srcs, dsts)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(reps):
+        srcs, dsts = sets[i % nsets]
+        ar.stream_(srcs, dsts)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del sets
+    torch.cuda.empty_cache()
+    return per_set / (ms * 1e-3) / 1e9, ms
+
+
+def host_mem_available_gib():
+    try:
+        with open("/proc/meminfo", encoding="ascii") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return round(int(line.split()[1]) / (1 << 20), 1)
+    except OSError:
+        pass
+    return None
+
+
 def oracle_allreduce(algo):
     """The oracle's message-passing simulation of `algo` (test infrastructure)."""
     import oracle
@@ -152,13 +229,16 @@ def oracle_allreduce(algo):
         return oracle.simulate_tree_allreduce
     if algo in ("halving_doubling", "halving_doubling_fused"):
         return oracle.simulate_hd_allreduce
-    if algo == "double_tree":
+    if algo in ("double_tree", "double_tree_fused"):
         return oracle.simulate_double_tree_allreduce
     return oracle.simulate_ring_allreduce
 
 
-def cpu_baseline(w, algo, sets_host, gpu_first, min_seconds):
-    """Time the CPU oracle on the workload; also check the GPU's first result."""
+def cpu_baseline(w, algo, sets_host, gpu_first, min_seconds, sample_count=None):
+    """Time the CPU oracle on the workload (or, when sample_count is given, on
+    the first sample_count elements of every rank: the same per-element work
+    at a size the host finishes in seconds); also check the GPU's first
+    result when it is given for the same input."""
     import numpy as np
     sim = oracle_allreduce(algo)
     reps, t_total = 0, 0.0
@@ -168,24 +248,54 @@ def cpu_baseline(w, algo, sets_host, gpu_first, min_seconds):
         out = sim(sets_host, w.dtype, w.op).state
         t_total += time.perf_counter() - t0
         reps += 1
-    ok = all(np.array_equal(np.ascontiguousarray(g).view(np.uint8),
-                            np.ascontiguousarray(o).view(np.uint8))
-             for g, o in zip(gpu_first, out))
+    ok = None
+    if gpu_first is not None:
+        ok = all(np.array_equal(np.ascontiguousarray(g).view(np.uint8),
+                                np.ascontiguousarray(o).view(np.uint8))
+                 for g, o in zip(gpu_first, out))
     per = t_total / reps
-    gbps = 2 * w.nranks * w.bytes_per_rank / per / 1e9
+    count = sample_count or w.count
+    nbytes = 2 * w.nranks * count * (w.bytes_per_rank // w.count)
+    gbps = nbytes / per / 1e9
+    what = (f"whole workload ({w.nranks} ranks x {w.count} {w.dtype}, {w.op})" if not sample_count
+            else f"the first {sample_count} of {w.count} {w.dtype} elements of each of the "
+                 f"{w.nranks} ranks (bucket set 0, {w.op}), an AllReduce of that count; the "
+                 f"whole workload needs {2 * w.nranks * w.bytes_per_rank / 2**30:.0f} GiB of "
+                 "host arrays for inputs and state")
     return {
         "value": round(gbps, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"whole workload ({w.nranks} ranks x {w.count} {w.dtype}, {w.op}) through "
-                   f"oracle.{sim.__name__}, {reps} run(s), {per:.3f} s each; numpy "
-                   "elementwise kernels, single thread"),
+        "sample": (f"{what} through oracle.{sim.__name__}, {reps} run(s), {per:.3f} s each; "
+                   "numpy elementwise kernels, single thread"),
         "seconds_per_allreduce": round(per, 4),
     }, ok
 
 
+def sampled_parity(w, algo, vals, idx, got):
+    """The oracle's per-position fold at sampled positions against the GPU
+    result there (full-size workloads whose whole oracle run would not fit)."""
+    import numpy as np
+
+    import oracle
+    per = -(-w.count // w.nranks)
+    if algo in ("ring_fused", "ring_step"):
+        want = oracle.ring_fold_at(vals, (idx // per).astype(np.int64), w.nranks, w.dtype, w.op)
+    elif algo in ("tree", "tree_fused"):
+        want = oracle.tree_fold_at(vals, w.dtype, w.op)
+    elif algo in ("halving_doubling", "halving_doubling_fused"):
+        want = oracle.hd_fold_at(vals, w.dtype, w.op)
+    else:
+        half = (w.count + 1) // 2
+        want = np.where(idx < half, oracle.dtree_fold_at(vals, 0, w.dtype, w.op),
+                        oracle.dtree_fold_at(vals, 1, w.dtype, w.op))
+    return bool(np.array_equal(np.ascontiguousarray(got).view(np.uint8),
+                               np.ascontiguousarray(want).view(np.uint8)))
+
+
 DTYPE_TAG = {"float32": "f32", "bfloat16": "bf16", "int32": "i32"}
+SAMPLE_COUNT = 1 << 22          # elements per rank of the CPU baseline's sample (large workloads)
 METRIC = "AllReduce GB/s + % of HBM peak, N=8 ranks \u00d7 25 MB fp32, 1 MI355X"
 
 
@@ -211,11 +321,12 @@ def sweep(args):
     import ring_allreduce_rs_amd as ar
     import workloads as W
     base = ("ring_step", "tree", "halving_doubling", "double_tree", "ring_fused", "tree_fused",
-            "halving_doubling_fused")
+            "halving_doubling_fused", "double_tree_fused")
     # "+graph": the same algorithm replayed from a library-recorded HIP graph
     algos = base + tuple(a + "+graph" for a in base[:4])
     launches = {"ring_step": 2 * 63, "tree": 6, "halving_doubling": 12, "double_tree": 12,
-                "ring_fused": 1, "tree_fused": 1, "halving_doubling_fused": 1}
+                "ring_fused": 1, "tree_fused": 1, "halving_doubling_fused": 1,
+                "double_tree_fused": 1}
     launches.update({a + "+graph": launches[a] for a in base[:4]})
     rows = {a: [] for a in algos}
     for w in W.SWEEP:
@@ -260,6 +371,65 @@ def sweep(args):
           flush=True)
 
 
+def size_sweep(w):
+    """The fused AllReduce against its access pattern's ceiling over sizes."""
+    import numpy as np
+    import torch
+
+    import ring_allreduce_rs_amd as ar
+    import workloads as W
+
+    def ev_time(fn, nsets, reps):
+        for i in range(nsets):
+            fn(i)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for i in range(reps):
+            fn(i % nsets)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e3
+
+    n, eb = w.nranks, w.itemsize
+    rows = []
+    for mib in (0.78125, 1.5625, 3.125, 6.25, 12.5, 25, 50, 100, 200, 400):
+        count = int(mib * (1 << 20)) // eb
+        kb = count * eb
+        ws = W.Workload(f"{w.name}@{mib}MiB", n, count, w.dtype, w.dist, w.op)
+        nsets = max(2, -(-4 * INFINITY_CACHE_BYTES // (n * kb)))
+        sets = [W.device_inputs(ws, seed=s) for s in range(nsets)]
+        calls = [ar.bind(ts, op=w.op, algo="ring_fused") for ts in sets]
+        reps = max(20, min(400, int(4e9 // (2 * n * kb))))
+        t_f = ev_time(lambda i: calls[i](), nsets, reps)
+        t_s = ev_time(lambda i: ar.stream_(sets[i], sets[i]), nsets, reps)
+        flat = [torch.empty(n * kb, dtype=torch.uint8, device="cuda") for _ in range(2 * nsets)]
+        t_c = ev_time(lambda i: ar.copy_(flat[2 * i], flat[2 * i + 1]), nsets, reps)
+        del sets, calls, flat
+        torch.cuda.empty_cache()
+        nbytes = 2 * n * kb
+        rows.append((nbytes, t_f, t_s, t_c))
+        print(json.dumps({"size_sweep": w.name, "MiB_per_rank": mib, "bytes": nbytes,
+                          "rotating_sets": nsets, "launches": reps,
+                          "fused_us": round(t_f, 2), "stream_in_place_us": round(t_s, 2),
+                          "copy_us": round(t_c, 2),
+                          "fused_frac": round(nbytes / t_f / 1e3 / HBM_PEAK_GBPS, 4),
+                          "stream_frac": round(nbytes / t_s / 1e3 / HBM_PEAK_GBPS, 4),
+                          "copy_frac": round(nbytes / t_c / 1e3 / HBM_PEAK_GBPS, 4),
+                          "fused_vs_stream": round(t_s / t_f, 4)}), flush=True)
+    r = np.array(rows)
+    sel = r[:, 0] >= 5e7
+    fit = {}
+    for j, name in ((1, "fused"), (2, "stream_in_place"), (3, "copy")):
+        b, a = np.polyfit(r[sel, 0], r[sel, j], 1)
+        fit[name] = {"a_us": round(a, 2), "GBps": round(1 / b / 1e3, 1),
+                     "frac": round(1 / b / 1e3 / HBM_PEAK_GBPS, 4)}
+    print(json.dumps({"size_sweep_fit": fit,
+                      "model": "T = a + bytes / GBps, fitted over sizes with >= 50 MB moved"}),
+          flush=True)
+
+
 def main():
     args, w = parse()
     if args.gpus != 1:
@@ -269,6 +439,8 @@ def main():
         sys.exit(2)
     if args.sweep:
         return sweep(args)
+    if args.size_sweep:
+        return size_sweep(w)
     import numpy as np
     import torch
 
@@ -278,7 +450,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.algo in ("tree", "halving_doubling", "double_tree") and w.nranks & (w.nranks - 1):
+    if args.algo not in ("ring_fused", "ring_step") and w.nranks & (w.nranks - 1):
         print(f"{args.algo} needs a power-of-two rank count", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
@@ -308,15 +480,40 @@ def main():
             sets.append(W.device_inputs(w, seed=args.seed + s))
     assert all(t.dtype == torch_dt for ts in sets for t in ts)
 
-    # first AllReduce of set 0, kept for the parity check in the CPU leg
+    # Full-size workloads too large for a whole oracle run: keep the first
+    # SAMPLE_COUNT inputs of every rank (the CPU baseline's sample) and the
+    # inputs at sampled positions (the parity check), both taken before the
+    # first AllReduce, which works in place.
+    sample_host = idx = vals = None
+    if host is None:
+        rng = np.random.Generator(np.random.PCG64(args.seed + 99))
+        idx = np.unique(np.concatenate([
+            rng.integers(0, w.count, size=4096),
+            np.array([0, w.count - 1, (w.count + 1) // 2 - 1, (w.count + 1) // 2]),
+            # both sides of every chunk boundary (ceil(count / N) apart)
+            np.array([c * -(-w.count // w.nranks) + d for c in range(1, w.nranks)
+                      for d in (-1, 0) if 0 <= c * -(-w.count // w.nranks) + d < w.count],
+                     dtype=np.int64)])).astype(np.int64)
+        ti = torch.from_numpy(idx).to("cuda")
+        vals = np.stack([download(t.index_select(0, ti)) for t in sets[0]])
+        if not args.no_cpu_baseline:
+            sample_host = [download(t[:SAMPLE_COUNT]) for t in sets[0]]
+
+    # first AllReduce of set 0, kept for the parity check
     ar.allreduce(sets[0], op=w.op, algo=args.algo)
     torch.cuda.synchronize()
     gpu_first = [download(t) for t in sets[0]] if host is not None else None
+    got_at = same = None
+    if host is None:
+        got_at = download(sets[0][0].index_select(0, torch.from_numpy(idx).to("cuda")))
+        same = all(torch.equal(t, sets[0][0]) for t in sets[0][1:])
 
     wall, ms = time_algo(ar, sets, w, args.algo, args.steps, args.warmup)
     alg_bytes = 2 * w.nranks * w.bytes_per_rank
     value = alg_bytes * args.steps / wall / 1e9
     t_step = wall / args.steps
+    stat_reps = max(20, min(args.steps, 200))
+    med, mn, _ = launch_stats(ar, sets, w, args.algo, stat_reps)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     key = f"{w.name}/{args.algo}"
     traffic = measured_traffic(key)
@@ -352,8 +549,14 @@ def main():
                        "tree": "k_tree_step",
                        "halving_doubling": "k_hd_rs_step/k_hd_ag_step",
                        "double_tree": "k_dtree_step", "tree_fused": "k_fused",
-                       "halving_doubling_fused": "k_fused"}[args.algo],
+                       "halving_doubling_fused": "k_fused",
+                       "double_tree_fused": "k_fused"}[args.algo],
             "us_per_launch": round(ms * 1e3, 3),
+            "us_per_launch_median": round(med * 1e3, 3),
+            "us_per_launch_min": round(mn * 1e3, 3),
+            "frac_median": round(alg_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "per_launch_pass": (f"{stat_reps} launches over the same bucket sets, each between "
+                                "its own two HIP events, after the timed region"),
             "algorithmic_bytes_per_launch": alg_bytes,
         },
         "gpu": torch.cuda.get_device_properties(0).name,
@@ -361,7 +564,7 @@ def main():
     if not args.no_others:
         others = {}
         for algo in ("ring_fused", "ring_step", "tree", "halving_doubling", "double_tree",
-                     "tree_fused", "halving_doubling_fused"):
+                     "tree_fused", "halving_doubling_fused", "double_tree_fused"):
             if algo == args.algo or (algo not in ("ring_fused", "ring_step")
                                      and w.nranks & (w.nranks - 1)):
                 continue
@@ -392,15 +595,44 @@ def main():
             }
         cg, cms = copy_ceiling(ar, w.nranks * w.bytes_per_rank)
         others["copy_ceiling"] = {"GBps": round(cg, 2), "bytes": 2 * w.nranks * w.bytes_per_rank,
-                                  "us": round(cms * 1e3, 2)}
+                                  "us": round(cms * 1e3, 2),
+                                  "frac_hbm_peak": round(cg / HBM_PEAK_GBPS, 4)}
+        # R-read / W-write streams of K bytes per buffer with the fused
+        # kernel's tiling and no reduction: N/N is the ceiling of the fused
+        # AllReduce's access pattern; the others separate reads from writes
+        n = w.nranks
+        streams = {}
+        for ns, nd, inpl in ((n, n, True), (n, n, False), (1, 1, False), (n, 0, False),
+                             (0, n, False), (n, 1, False), (1, n, False)):
+            if ns + nd > 64 and not inpl:
+                continue
+            g, sms = stream_ceiling(ar, ns, nd, w.bytes_per_rank, in_place=inpl)
+            streams[f"{ns}R{nd}W" + ("_in_place" if inpl else "")] = {
+                "GBps": round(g, 2), "us": round(sms * 1e3, 2),
+                "frac_hbm_peak": round(g / HBM_PEAK_GBPS, 4)}
+        others["stream_ceiling"] = streams
+        if args.algo.endswith("_fused"):
+            # event time of the in-place N-read / N-write stream over the
+            # fused AllReduce's mean event time: 1.0 = at that ceiling
+            others["fused_vs_stream"] = round(streams[f"{n}R{n}W_in_place"]["us"] / (ms * 1e3), 4)
         out["others"] = others
-    if not args.no_cpu_baseline and host is not None:
-        cb, ok = cpu_baseline(w, args.algo, host, gpu_first, args.cpu_seconds)
+    parity = None
+    if not args.no_cpu_baseline:
+        # the CPU leg: the oracle timed, and the GPU's first result checked
+        # against it (whole, or at the sampled positions)
+        if host is not None:
+            cb, ok = cpu_baseline(w, args.algo, host, gpu_first, args.cpu_seconds)
+            parity = "bitwise (whole workload)" if ok else "MISMATCH"
+        else:
+            cb, _ = cpu_baseline(w, args.algo, sample_host, None, args.cpu_seconds,
+                                 sample_count=SAMPLE_COUNT)
+            parity = (f"bitwise at {idx.size} sampled positions (rank 0), every rank identical"
+                      if sampled_parity(w, args.algo, vals, idx, got_at) and same
+                      else "MISMATCH")
         cb["host_cpus"] = os.cpu_count()
+        cb["host_mem_available_GiB"] = host_mem_available_gib()
         out["cpu_baseline"] = cb
-        out["parity_vs_oracle"] = "bitwise" if ok else "MISMATCH"
-    elif not args.no_cpu_baseline:
-        out["cpu_baseline"] = None
+    out["parity_vs_oracle"] = parity
     print(json.dumps(out), flush=True)
 
 

@@ -290,7 +290,8 @@ ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes);
  * mixes separate the cost of read streams from that of write streams.
  * src and dst are HOST arrays of DEVICE pointers (read during the call),
  * every buffer 16-byte aligned, device memory of the context's device, no two
- * overlapping; bytes a multiple of 16; 1 <= nsrc + ndst <= AR_MAX_RANKS.
+ * overlapping, except that dst[i] may equal src[i] (in place, as an
+ * AllReduce works); bytes a multiple of 16; 1 <= nsrc + ndst <= AR_MAX_RANKS.
  * Enqueued on the context's stream.  Errors: AR_ERR_INVALID_ARG for any of
  * the above, AR_ERR_RUNTIME if the launch fails. */
 ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* dst, int ndst,

@@ -157,7 +157,7 @@ def copy_(dst, src):
 def stream_(srcs, dsts):
     """Calibration stream (ar_stream): the XOR of the source tensors written to
     every destination tensor, all of one byte size, on the current stream."""
-    bufs = list(srcs) + list(dsts)
+    bufs = list(srcs) + list(dsts)      # dsts[i] may be srcs[i] itself (in place)
     if not bufs:
         raise ValueError("stream_ needs at least one buffer")
     nbytes = bufs[0].numel() * bufs[0].element_size()

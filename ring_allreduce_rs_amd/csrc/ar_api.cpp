@@ -778,10 +778,14 @@ ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* 
         if (bytes % 16) return fail(ctx, AR_ERR_INVALID_ARG, "bytes %zu is not a multiple of 16",
                                     bytes);
         if (bytes == 0) return AR_OK;
-        // every buffer: device memory of this device, 16-byte aligned, no overlap
+        // every buffer: device memory of this device, 16-byte aligned, no
+        // overlap -- except that dst[i] may be src[i] itself (the in-place
+        // pattern of an AllReduce: each block reads its tile of every source
+        // before it writes, and blocks own disjoint tiles)
         std::vector<void*> all;
         for (int i = 0; i < nsrc; ++i) all.push_back(const_cast<void*>(src[i]));
-        for (int i = 0; i < ndst; ++i) all.push_back(dst[i]);
+        for (int i = 0; i < ndst; ++i)
+            if (!(i < nsrc && dst[i] == src[i])) all.push_back(dst[i]);
         for (size_t i = 0; i < all.size(); ++i)
             if (reinterpret_cast<uintptr_t>(all[i]) & 15u)
                 return fail(ctx, AR_ERR_INVALID_ARG, "buffer %zu is not 16-byte aligned", i);

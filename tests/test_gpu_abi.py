@@ -179,6 +179,21 @@ def test_calibration_stream_writes_the_xor(nsrc, ndst):
         assert torch.equal(s, k)
 
 
+def test_calibration_stream_in_place():
+    """dst[i] == src[i]: every buffer ends with the XOR of all the inputs."""
+    n, nbytes = 8, 5 * 4096 + 32
+    g = torch.Generator(device="cpu").manual_seed(7)
+    bufs = [torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32).cuda()
+            for _ in range(n)]
+    want = np.zeros(nbytes // 4, np.int32)
+    for b in bufs:
+        want ^= b.cpu().numpy()
+    ar.stream_(bufs, bufs)
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert np.array_equal(b.cpu().numpy(), want)
+
+
 def test_calibration_stream_rejects_bad_arguments(ctx):
     a = torch.zeros(1024, dtype=torch.int32, device="cuda")
     b = torch.zeros(1024, dtype=torch.int32, device="cuda")
@@ -189,6 +204,7 @@ def test_calibration_stream_rejects_bad_arguments(ctx):
         "bytes not a multiple of 16": lambda: ctx.stream_ptrs([pa], [pb], 4000 + 8),
         "misaligned": lambda: ctx.stream_ptrs([pa + 4], [pb], 1024),
         "overlap": lambda: ctx.stream_ptrs([pa], [pa + 16], 1024),
+        "dst is another source": lambda: ctx.stream_ptrs([pa, pb], [pb], 1024),
         "past allocation": lambda: ctx.stream_ptrs([pa], [pb], 8192),
         "host pointer": lambda: ctx.stream_ptrs([np.zeros(256, np.int32).ctypes.data], [pb],
                                                 1024),

@@ -2,12 +2,14 @@
 benchmark times.
 
 Where the oracle finishes in seconds it runs on the whole input (4-rank
-int32, the 25 MiB DDP bucket, the two small sweep points); elsewhere it
-computes sampled positions one by one (random positions plus the
-neighbourhood of every chunk boundary, where heads, tails and straddling
-16-byte units live), and whole-array properties are checked on the GPU: all
-ranks identical, fused == per-step bitwise, exact integer / max results
-against an independent torch reduction.
+int32, the 25 MiB DDP bucket, the two small sweep points).  The two
+multi-GiB workloads (8 x 2^30 bf16, 16 x 268,435,459) are checked against the
+oracle over the whole array too, streamed through the host in slices (each
+slice's inputs and results downloaded, the oracle's per-position fold run on
+it, several slices at a time on the host's cores), besides sampled positions
+(random positions plus the neighbourhood of every chunk boundary, where
+heads, tails and straddling 16-byte units live).  Whole-array properties are
+also checked on the GPU: all ranks identical, fused == per-step bitwise.
 """
 
 import sys
@@ -19,8 +21,8 @@ import torch
 import oracle
 import ring_allreduce_rs_amd as ar
 import workloads as W
-from tests.gpu_helpers import (assert_bits_equal, chunk_ids, gather, sample_positions, to_gpu,
-                               to_np)
+from tests.gpu_helpers import (assert_bits_equal, bits, chunk_ids, gather, sample_positions,
+                               to_gpu, to_np)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -41,6 +43,36 @@ def clone_all(ts):
 
 def ranks_identical(ts):
     return all(torch.equal(t, ts[0]) for t in ts[1:])
+
+
+SLICE = 1 << 23          # elements per slice of the streamed whole-array checks
+
+
+def whole_array_vs_oracle(inputs, result, want_at, what, workers=12):
+    """Compare ``result`` (one rank's output, on the GPU) with the oracle over
+    every position.  ``inputs`` are the untouched input tensors; for each
+    slice [lo, hi) the (N, hi - lo) input block and the result slice are
+    downloaded and ``want_at(values, lo)`` (an oracle function of the block)
+    must equal the result bit for bit.  Slices run ``workers`` at a time
+    (numpy releases the interpreter lock in its kernels)."""
+    from concurrent.futures import ThreadPoolExecutor
+    count = result.numel()
+
+    def one(lo):
+        hi = min(lo + SLICE, count)
+        vals = np.stack([to_np(t[lo:hi]) for t in inputs])
+        got = to_np(result[lo:hi])
+        want = want_at(vals, lo)
+        g = np.ascontiguousarray(got).view(np.uint8)
+        w_ = np.ascontiguousarray(want).view(np.uint8)
+        if not np.array_equal(g, w_):
+            bad = np.nonzero(bits(got) != bits(want))[0]
+            return f"{what}: slice at {lo}: {bad.size} elements differ, first at {lo + int(bad[0])}"
+        return None
+
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        errs = [e for e in pool.map(one, range(0, count, SLICE)) if e]
+    assert not errs, errs[:3]
 
 
 def test_small_int32_config():
@@ -107,6 +139,7 @@ def test_bf16_2gib_config():
     a = W.device_inputs(w, seed=0)
     idx = sample_positions(w.count, w.nranks, k=8192, seed=1)
     vals = gather(a, idx)
+    pristine = clone_all(a)
     b = clone_all(a)
     say("bf16 2GiB: ring_step")
     run(a, "sum", "ring_step")
@@ -123,7 +156,14 @@ def test_bf16_2gib_config():
     gamma = (w.nranks - 1) * up / (1 - (w.nranks - 1) * up)
     err = np.abs(oracle.bf16_to_f32(want).astype(np.float64) - f.sum(axis=0))
     assert (err <= gamma * np.abs(f).sum(axis=0)).all()
-    del a, b
+    say("bf16 2GiB: whole array against the oracle")
+    per = -(-w.count // w.nranks)
+    whole_array_vs_oracle(
+        pristine, b[0],
+        lambda v, lo: oracle.ring_fold_at(v, (np.arange(lo, lo + v.shape[1]) // per), w.nranks,
+                                          "bfloat16", "sum"),
+        "bf16 2GiB fused")
+    del a, b, pristine
     torch.cuda.empty_cache()
 
 
@@ -194,6 +234,7 @@ def test_ragged_config(w):
     a = W.device_inputs(w, seed=0)
     idx = sample_positions(w.count, w.nranks, k=8192, seed=3)
     vals = gather(a, idx)
+    pristine = clone_all(a)
     # independent whole-array reference computed by torch before the call
     if w.op == "max":
         ref = a[0].clone()
@@ -215,5 +256,12 @@ def test_ragged_config(w):
         assert torch.equal(b[r], ref), f"ring_step rank {r} differs"
     want = (oracle.exact_max(vals, w.dtype) if w.op == "max" else oracle.exact_int_sum(vals))
     assert_bits_equal(gather(a[:1], idx)[0], want, "sampled positions")
-    del a, b, ref
+    del b, ref
+    say(f"ragged {w.name}: whole array against the oracle")
+    whole_array_vs_oracle(
+        pristine, a[0],
+        (lambda v, lo: oracle.exact_max(list(v), w.dtype)) if w.op == "max"
+        else (lambda v, lo: oracle.exact_int_sum(list(v))),
+        f"{w.name} fused")
+    del a, pristine
     torch.cuda.empty_cache()
