@@ -25,7 +25,8 @@
  *    the identity).
  *  - No call allocates device memory for data: the pointer table travels by
  *    value in the kernel arguments.  (With ar_set_graphs on, the HIP runtime
- *    allocates what an instantiated graph needs, once per recorded graph.)
+ *    allocates what an instantiated graph needs, once per recorded graph; the
+ *    first ar_check on a context allocates the checker's 80 KiB scratch.)
  *  - No C++ exception crosses this interface.  A context is not thread-safe;
  *    use one per host thread / stream.
  *  - ar_last_error(ctx) describes the most recent failure on that context.
@@ -297,6 +298,39 @@ ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes);
 ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* dst, int ndst,
                     size_t bytes);
 
+/* On-device check of an AllReduce result, a test utility: the whole array is
+ * checked where it lies, without copying it to the host.  An AllReduce leaves
+ * every participant with the same data ("AllReduce", compassingai.com,
+ * section 3 技术原理), and a floating-point SUM is judged against the exact
+ * sum through an error bound.
+ *  mismatched      positions i in [0, count) where some bufs[r][i] differs bit
+ *                  for bit from bufs[0][i]
+ *  first_mismatch  the smallest such i (count if there is none)
+ *  over_bound      with ref: positions where |bufs[0][i] - ref[i]| (binary64,
+ *                  the element widened exactly) exceeds bound[i] (bound given)
+ *                  or is NaN
+ *  max_abs_err     with ref: the largest |bufs[0][i] - ref[i]|; NaN if any
+ *                  difference is NaN; 0 without ref
+ * ref and bound: NULL, or DEVICE arrays of `count` binary64 values (bound
+ * needs ref).  result: a DEVICE pointer to one ar_check_result (8-byte
+ * aligned), written asynchronously on the context's stream: synchronise
+ * before reading it.  bufs: as for ar_allreduce (they are only read).  The
+ * per-block partial records live in a scratch array of 2048 records that the
+ * context allocates on its first ar_check and frees in ar_destroy.  Errors:
+ * AR_ERR_INVALID_ARG for bad buffers, a NULL or misplaced result, bound
+ * without ref, or ref/bound not holding count doubles of device memory;
+ * AR_ERR_NO_MEMORY if the scratch array cannot be allocated; AR_ERR_RUNTIME
+ * if a launch fails. */
+typedef struct ar_check_result {
+    unsigned long long mismatched;
+    unsigned long long first_mismatch;
+    unsigned long long over_bound;
+    double max_abs_err;
+} ar_check_result;
+
+ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
+                   const double* ref, const double* bound, ar_check_result* result);
+
 /* Static description of a status code (never NULL). */
 const char* ar_status_string(ar_status s);
 
@@ -305,7 +339,8 @@ const char* ar_status_string(ar_status s);
 const char* ar_last_error(const ar_ctx* ctx);
 
 /* Destroy a context.  ar_destroy(NULL) is a no-op returning AR_OK.  Work
- * already enqueued is not waited for. */
+ * already enqueued is not waited for, except that a context which ran
+ * ar_check first waits for its stream, then frees the checker's scratch. */
 ar_status ar_destroy(ar_ctx* ctx);
 
 #ifdef __cplusplus

@@ -25,7 +25,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
     "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "dtree_step", "copy_", "stream_",
-    "chunk_range", "bind",
+    "check", "chunk_range", "bind",
     "context", "LIB_PATH", "predict_us", "auto_algo", "set_graphs",
 ]
 
@@ -152,6 +152,29 @@ def copy_(dst, src):
         raise ValueError("copy_ needs equal byte sizes")
     context(src.device.index or 0).copy_ptrs(dst.data_ptr(), src.data_ptr(), nbytes)
     return dst
+
+
+def check(tensors, ref=None, bound=None) -> dict:
+    """On-device check of an AllReduce result (ar_check): positions where some
+    rank's bits differ from rank 0's, the first of them, and -- given a
+    float64 reference (and per-position bounds) on the same device -- the
+    largest |rank 0 - ref| and the positions over their bound.  Waits for the
+    result on the current stream."""
+    torch = _torch()
+    ts, dt, count, dev = _check(tensors)
+    for name, t in (("ref", ref), ("bound", bound)):
+        if t is not None and (t.dtype != torch.float64 or t.numel() != count
+                              or t.device != ts[0].device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float64 tensor of {count} elements "
+                             "on the buffers' device")
+    out = torch.zeros(4, dtype=torch.int64, device=ts[0].device)
+    context(dev).check_ptrs([t.data_ptr() for t in ts], count, dt,
+                            ref.data_ptr() if ref is not None else 0,
+                            bound.data_ptr() if bound is not None else 0, out.data_ptr())
+    torch.cuda.current_stream(ts[0].device).synchronize()
+    v = out.cpu()
+    return {"mismatched": int(v[0]), "first_mismatch": int(v[1]), "over_bound": int(v[2]),
+            "max_abs_err": float(v[3:4].view(torch.float64)[0])}
 
 
 def stream_(srcs, dsts):

@@ -33,7 +33,7 @@ EXPORTS = (
     "ar_create", "ar_set_stream", "ar_set_graphs", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
     "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
     "ar_dtree_step",
-    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy", "ar_stream",
+    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy", "ar_stream", "ar_check",
     "ar_status_string", "ar_last_error", "ar_destroy",
 )
 
@@ -81,6 +81,7 @@ def _load() -> ctypes.CDLL:
         "ar_auto_algo": ([i, sz, i, ctypes.POINTER(i)], i),
         "ar_copy": ([vp, vp, vp, sz], i),
         "ar_stream": ([vp, pp, i, pp, i, sz], i),
+        "ar_check": ([vp, pp, i, sz, i, vp, vp, vp], i),
         "ar_status_string": ([i], cp),
         "ar_last_error": ([vp], cp),
         "ar_destroy": ([vp], i),
@@ -208,6 +209,10 @@ class Context:
 
     def copy_ptrs(self, dst, src, nbytes):
         self._check(lib.ar_copy(self._h, dst, src, nbytes), "ar_copy")
+
+    def check_ptrs(self, ptrs, count, dtype, ref, bound, result):
+        self._check(lib.ar_check(self._h, _ptr_array(ptrs), len(ptrs), count, DTYPES[dtype],
+                                 ref or None, bound or None, result or None), "ar_check")
 
     def stream_ptrs(self, srcs, dsts, nbytes):
         self._check(lib.ar_stream(self._h, _ptr_array(srcs), len(srcs), _ptr_array(dsts),

@@ -57,6 +57,9 @@ struct ar_ctx {
     size_t graph_max_bytes = 0;   // replay collectives of at most this many bytes per rank
     hipStream_t capture = nullptr;
     std::vector<GraphEntry> graph_cache;
+    // ar_check's per-block partial records (kCheckMaxBlocks of them),
+    // allocated on the first ar_check
+    arlib::CheckPartial* check_part = nullptr;
 };
 
 static constexpr size_t kCheckedSets = 32;
@@ -287,6 +290,33 @@ ar_status check_buffers(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
             if (ctx->checked[i].stamp < ctx->checked[oldest].stamp) oldest = i;
         ctx->checked[oldest] = std::move(entry);
     }
+    return AR_OK;
+}
+
+// A device array of `bytes` bytes at p: device memory of ctx->device, inside
+// its allocation (fail closed, like the rank buffers).
+ar_status check_device_span(ar_ctx* ctx, const void* p, size_t bytes, const char* what) {
+    hipPointerAttribute_t at;
+    std::memset(&at, 0, sizeof at);
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_INVALID_ARG, "%s is not a device pointer", what);
+    }
+    if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged)
+        return fail(ctx, AR_ERR_INVALID_ARG, "%s is not device memory", what);
+    if (at.device != ctx->device)
+        return fail(ctx, AR_ERR_INVALID_ARG, "%s lives on device %d, context on %d", what,
+                    at.device, ctx->device);
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess || !base) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_INVALID_ARG, "%s: cannot determine its allocation", what);
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    if (q < b || bytes > size || q - b > size - bytes)
+        return fail(ctx, AR_ERR_INVALID_ARG, "%s: %zu bytes run past the end of its allocation",
+                    what, bytes);
     return AR_OK;
 }
 
@@ -809,6 +839,64 @@ ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* 
     }
 }
 
+ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
+                   const double* ref, const double* bound, ar_check_result* result) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    try {
+        if (!result) return fail(ctx, AR_ERR_INVALID_ARG, "result is NULL");
+        if (reinterpret_cast<uintptr_t>(result) & 7u)
+            return fail(ctx, AR_ERR_INVALID_ARG, "result is not 8-byte aligned");
+        if (bound && !ref) return fail(ctx, AR_ERR_INVALID_ARG, "bound given without ref");
+        bool vec;
+        unsigned mis;
+        ar_status s = check_buffers(ctx, bufs, nranks, count, (int)dtype, &vec, &mis);
+        if (s != AR_OK) return s;
+        s = check_device_span(ctx, result, sizeof(ar_check_result), "result");
+        if (s != AR_OK) return s;
+        if (count > 0) {
+            if (count > SIZE_MAX / sizeof(double))
+                return fail(ctx, AR_ERR_INVALID_ARG, "count %zu overflows the reference", count);
+            if (ref && (reinterpret_cast<uintptr_t>(ref) & 7u))
+                return fail(ctx, AR_ERR_INVALID_ARG, "ref is not 8-byte aligned");
+            if (bound && (reinterpret_cast<uintptr_t>(bound) & 7u))
+                return fail(ctx, AR_ERR_INVALID_ARG, "bound is not 8-byte aligned");
+            if (ref && (s = check_device_span(ctx, ref, count * sizeof(double), "ref")) != AR_OK)
+                return s;
+            if (bound && (s = check_device_span(ctx, bound, count * sizeof(double), "bound")) != AR_OK)
+                return s;
+        }
+        DeviceGuard g(ctx->device);
+        if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
+        if (!ctx->check_part) {
+            void* p = nullptr;
+            if (hipMalloc(&p, sizeof(arlib::CheckPartial) * arlib::kCheckMaxBlocks) != hipSuccess ||
+                !p) {
+                (void)hipGetLastError();
+                return fail(ctx, AR_ERR_NO_MEMORY, "cannot allocate the checker's scratch array");
+            }
+            ctx->check_part = static_cast<arlib::CheckPartial*>(p);
+        }
+        arlib::CheckArgs a;
+        a.t = table_of(bufs, nranks);
+        a.count = count;
+        a.n = nranks;
+        a.dtype = (int)dtype;
+        a.eb = (int)elem_bytes(dtype);
+        a.ref = count ? ref : nullptr;
+        a.bound = count ? bound : nullptr;
+        const hipError_t e = arlib::launch_check(a, ctx->check_part, result, ctx->stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ctx, AR_ERR_RUNTIME, "check launch failed: %s", hipGetErrorString(e));
+        }
+        return AR_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(ctx, AR_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
+    }
+}
+
 const char* ar_status_string(ar_status s) {
     switch (s) {
         case AR_OK: return "AR_OK";
@@ -826,10 +914,15 @@ const char* ar_last_error(const ar_ctx* ctx) {
 
 ar_status ar_destroy(ar_ctx* ctx) {
     if (!ctx) return AR_OK;
-    if (!ctx->graph_cache.empty() || ctx->capture) {
+    if (!ctx->graph_cache.empty() || ctx->capture || ctx->check_part) {
         DeviceGuard g(ctx->device);
         clear_graphs(ctx);
         if (ctx->capture) (void)hipStreamDestroy(ctx->capture);
+        // the checker's scratch may still be in use by enqueued work
+        if (ctx->check_part) {
+            (void)hipStreamSynchronize(ctx->stream);
+            (void)hipFree(ctx->check_part);
+        }
         (void)hipGetLastError();
     }
     delete ctx;

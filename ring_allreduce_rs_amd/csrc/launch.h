@@ -78,4 +78,29 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t str
 hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
                          size_t bytes, hipStream_t stream);
 
+// On-device result checker (check.hip): pass 1 writes one partial record per
+// block (at most kCheckMaxBlocks) to `part`, pass 2 folds them into `out`.
+constexpr int kCheckThreads = 256;
+constexpr unsigned kCheckMaxBlocks = 2048;
+struct CheckArgs {
+    RankTable t;
+    size_t count;
+    int n;
+    int dtype;           // ar_dtype
+    int eb;              // element bytes
+    const double* ref;   // NULL: no error check
+    const double* bound; // NULL: no bound check (needs ref)
+};
+struct CheckPartial {
+    unsigned long long mismatched;
+    unsigned long long first;
+    unsigned long long over;
+    double max_err;
+    unsigned nan;
+    unsigned pad;
+};
+unsigned check_blocks(size_t count);   // blocks of pass 1 (partial records written)
+hipError_t launch_check(const CheckArgs& a, CheckPartial* part, ar_check_result* out,
+                        hipStream_t s);
+
 }  // namespace arlib

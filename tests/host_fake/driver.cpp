@@ -28,6 +28,8 @@ int g_fail = 0;
 constexpr uintptr_t kBase = uintptr_t(1) << 44;
 constexpr uintptr_t kStride = uintptr_t(1) << 43;   // 8 TiB per rank
 constexpr int kMaxN = AR_MAX_RANKS;
+// device-0 memory after the rank buffers, for the checker's reference and result
+constexpr uintptr_t kAux = kBase + (uintptr_t)kMaxN * kStride;
 
 void* rank_addr(int r, size_t byte_shift) {
     return reinterpret_cast<void*>(kBase + (uintptr_t)r * kStride + byte_shift);
@@ -460,10 +462,47 @@ void check_graphs(ar_ctx* ctx) {
 
 }  // namespace
 
+// ------------------------------------------------------------- checker
+void check_checker(ar_ctx* ctx) {
+    FakeCounters& fc = fake_counters();
+    void* bufs[kMaxN];
+    for (int r = 0; r < kMaxN; ++r) bufs[r] = rank_addr(r, 0);
+    auto* res = reinterpret_cast<ar_check_result*>(kAux);
+    const auto* ref = reinterpret_cast<const double*>(kAux + 4096);
+    const auto* bound = reinterpret_cast<const double*>(kAux + (kStride >> 1));
+    // an address the fake runtime does not know (not device memory)
+    const auto* host_ref = reinterpret_cast<const double*>(uintptr_t(1) << 40);
+    const long l0 = fc.kernel_launches, a0 = fc.device_allocs;
+    auto bad = [&](ar_status st, const char* what) {
+        CHECK(st == AR_ERR_INVALID_ARG, "%s: status %d", what, (int)st);
+    };
+    bad(ar_check(ctx, bufs, 8, 100, AR_FLOAT32, nullptr, nullptr, nullptr), "NULL result");
+    bad(ar_check(ctx, bufs, 8, 100, AR_FLOAT32, nullptr, nullptr,
+                 reinterpret_cast<ar_check_result*>(kAux + 4)), "misaligned result");
+    bad(ar_check(ctx, bufs, 8, 100, AR_FLOAT32, nullptr, bound, res), "bound without ref");
+    bad(ar_check(ctx, bufs, 8, 4, AR_FLOAT32, host_ref, nullptr, res), "host ref");
+    bad(ar_check(ctx, bufs, 8, 100, AR_FLOAT32,
+                 reinterpret_cast<const double*>(kAux + kStride - 64), nullptr, res), "short ref");
+    bad(ar_check(ctx, bufs, 8, 100, AR_FLOAT32, ref,
+                 reinterpret_cast<const double*>(kAux + kStride - 64), res), "short bound");
+    bad(ar_check(ctx, bufs, 8, 100, AR_FLOAT32, ref, nullptr,
+                 reinterpret_cast<ar_check_result*>(kBase - kStride)), "result on device 1");
+    bad(ar_check(ctx, bufs, 0, 100, AR_FLOAT32, nullptr, nullptr, res), "no ranks");
+    bad(ar_check(ctx, bufs, 8, 100, (ar_dtype)9, nullptr, nullptr, res), "bad dtype");
+    CHECK(fc.kernel_launches == l0 && fc.device_allocs == a0, "a rejected check launched");
+    CHECK(ar_check(ctx, bufs, 8, 100000, AR_BFLOAT16, ref, bound, res) == AR_OK, "check");
+    CHECK(fc.kernel_launches == l0 + 2 && fc.device_allocs == a0 + 1, "check: 2 launches, 1 alloc");
+    CHECK(ar_check(ctx, bufs, 3, 7, AR_INT32, nullptr, nullptr, res) == AR_OK, "check again");
+    CHECK(fc.kernel_launches == l0 + 4 && fc.device_allocs == a0 + 1, "scratch kept");
+    CHECK(ar_check(ctx, bufs, 3, 0, AR_INT32, nullptr, nullptr, res) == AR_OK, "check count 0");
+    CHECK(fc.kernel_launches == l0 + 5, "count 0: the final pass only");
+}
+
 int main() {
-    // rank buffers of device 0, and one range on device 1
+    // rank buffers of device 0, one range on device 1, the checker's arrays
     for (int r = 0; r < kMaxN; ++r) fake_register(rank_addr(r, 0), kStride, 0);
     fake_register(reinterpret_cast<void*>(kBase - kStride), kStride, 1);
+    fake_register(reinterpret_cast<void*>(kAux), kStride, 0);
 
     check_chunk_range();
     check_cost_model();
@@ -481,6 +520,7 @@ int main() {
         check_validation(ctx);
         check_launches(ctx);
         check_graphs(ctx);
+        check_checker(ctx);
         // leave a few graphs recorded: ar_destroy must release them
         CHECK(ar_set_graphs(ctx, SIZE_MAX) == AR_OK, "graphs on");
         void* bufs[kMaxN];
@@ -491,8 +531,10 @@ int main() {
     }
     const FakeCounters& fc = fake_counters();
     CHECK(fc.execs_created == fc.execs_destroyed && fc.events_created == fc.events_destroyed &&
-              fc.streams_created == fc.streams_destroyed,
-          "ar_destroy left graphs, events or streams behind");
+              fc.streams_created == fc.streams_destroyed && fc.device_allocs == fc.device_frees,
+          "ar_destroy left graphs, events, streams or scratch behind");
+    CHECK(fc.device_allocs == 1 && fc.stream_syncs >= 1, "checker scratch: %ld allocs, %ld syncs",
+          fc.device_allocs, fc.stream_syncs);
     const char* msg = nullptr;
     CHECK(fake_coverage_ok(&msg), "launch coverage: %s", msg);
     std::printf("launches %ld, graph launches %ld, captures %ld, evictions %ld\n",

@@ -187,6 +187,15 @@ hipError_t launch_stream(const void* const*, int, void* const*, int, size_t, hip
     ++g_count.kernel_launches;
     return hipSuccess;
 }
+unsigned check_blocks(size_t count) {
+    const size_t want = (count + kCheckThreads - 1) / kCheckThreads;
+    return (unsigned)(want == 0 ? 1 : want < kCheckMaxBlocks ? want : kCheckMaxBlocks);
+}
+hipError_t launch_check(const CheckArgs& a, CheckPartial* part, ar_check_result* out, hipStream_t) {
+    g_count.kernel_launches += a.count > 0 ? 2 : 1;
+    if (!part || !out) coverage_fail("checker launched without scratch or result", Args{}, dim3(0));
+    return hipSuccess;
+}
 }  // namespace arlib
 
 // ------------------------------------------------------------- HIP runtime
@@ -301,6 +310,23 @@ hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
     return hipSuccess;
 }
 hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
+hipError_t hipMalloc(void** p, size_t size) {
+    // host memory stands in for the allocation; kernels never run here
+    *p = new char[size ? size : 1];
+    ++g_count.device_allocs;
+    return hipSuccess;
+}
+hipError_t hipFree(void* p) {
+    if (p) {
+        delete[] static_cast<char*>(p);
+        ++g_count.device_frees;
+    }
+    return hipSuccess;
+}
+hipError_t hipStreamSynchronize(hipStream_t) {
+    ++g_count.stream_syncs;
+    return hipSuccess;
+}
 hipError_t hipEventSynchronize(hipEvent_t) {
     ++g_count.event_syncs;
     return hipSuccess;

@@ -19,6 +19,7 @@ struct FakeCounters {
     long execs_created = 0, execs_destroyed = 0;
     long graph_launches = 0;
     long events_created = 0, events_destroyed = 0, event_syncs = 0;
+    long device_allocs = 0, device_frees = 0, stream_syncs = 0;
 };
 
 // Registers [base, base + size) as device memory of `device` (never touched).

@@ -70,8 +70,11 @@ def whole_array_vs_oracle(inputs, result, want_at, what, workers=12):
             return f"{what}: slice at {lo}: {bad.size} elements differ, first at {lo + int(bad[0])}"
         return None
 
+    starts = range(0, count, SLICE)
     with ThreadPoolExecutor(max_workers=workers) as pool:
-        errs = [e for e in pool.map(one, range(0, count, SLICE)) if e]
+        res = list(pool.map(one, starts))
+    assert len(res) == -(-count // SLICE)          # every slice was compared
+    errs = [e for e in res if e]
     assert not errs, errs[:3]
 
 
