@@ -331,6 +331,24 @@ typedef struct ar_check_result {
 ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
                    const double* ref, const double* bound, ar_check_result* result);
 
+/* ar_check for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, validation and results as ar_check, and the same kernels; the
+ * partial records live in a device-resident array of AR_CHECK_MAX_RECORDS
+ * records (80 KiB) that each GPU the library runs on holds until the process
+ * ends, located once per device by ar_create.  The call allocates nothing
+ * (no hipMalloc, no hipFree) and launches two kernels.  Every count fits: the
+ * first pass never uses more than AR_CHECK_MAX_RECORDS blocks, each writing
+ * the one record the second pass reads, so no state carries over between
+ * calls.  All calls on one GPU share that array: calls that overlap on one
+ * GPU (several streams or contexts at once) race and give wrong results, so
+ * run them one after another.  Errors: as ar_check, and AR_ERR_RUNTIME if
+ * the array could not be located on this device when the context was made. */
+#define AR_CHECK_MAX_RECORDS 2048
+ar_status ar_check_noalloc(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                           ar_dtype dtype, const double* ref, const double* bound,
+                           ar_check_result* result);
+
 /* Static description of a status code (never NULL). */
 const char* ar_status_string(ar_status s);
 

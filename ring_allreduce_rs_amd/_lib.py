@@ -33,7 +33,7 @@ EXPORTS = (
     "ar_create", "ar_set_stream", "ar_set_graphs", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
     "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
     "ar_dtree_step",
-    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy", "ar_stream", "ar_check",
+    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy", "ar_stream", "ar_check", "ar_check_noalloc",
     "ar_status_string", "ar_last_error", "ar_destroy",
 )
 
@@ -82,6 +82,7 @@ def _load() -> ctypes.CDLL:
         "ar_copy": ([vp, vp, vp, sz], i),
         "ar_stream": ([vp, pp, i, pp, i, sz], i),
         "ar_check": ([vp, pp, i, sz, i, vp, vp, vp], i),
+        "ar_check_noalloc": ([vp, pp, i, sz, i, vp, vp, vp], i),
         "ar_status_string": ([i], cp),
         "ar_last_error": ([vp], cp),
         "ar_destroy": ([vp], i),
@@ -213,6 +214,11 @@ class Context:
     def check_ptrs(self, ptrs, count, dtype, ref, bound, result):
         self._check(lib.ar_check(self._h, _ptr_array(ptrs), len(ptrs), count, DTYPES[dtype],
                                  ref or None, bound or None, result or None), "ar_check")
+
+    def check_noalloc_ptrs(self, ptrs, count, dtype, ref, bound, result):
+        self._check(lib.ar_check_noalloc(self._h, _ptr_array(ptrs), len(ptrs), count,
+                                         DTYPES[dtype], ref or None, bound or None,
+                                         result or None), "ar_check_noalloc")
 
     def stream_ptrs(self, srcs, dsts, nbytes):
         self._check(lib.ar_stream(self._h, _ptr_array(srcs), len(srcs), _ptr_array(dsts),

@@ -60,6 +60,10 @@ struct ar_ctx {
     // ar_check's per-block partial records (kCheckMaxBlocks of them),
     // allocated on the first ar_check
     arlib::CheckPartial* check_part = nullptr;
+    // ar_check_noalloc's records: the device-resident array on this
+    // context's device, looked up in ar_create (NULL if that failed)
+    arlib::CheckPartial* check_static = nullptr;
+    std::string check_static_error;
 };
 
 static constexpr size_t kCheckedSets = 32;
@@ -679,6 +683,18 @@ ar_status ar_create(ar_ctx** out, int device, void* stream) {
     if (!c) return fail(nullptr, AR_ERR_NO_MEMORY, "cannot allocate the context");
     c->device = device;
     c->stream = reinterpret_cast<hipStream_t>(stream);
+    {
+        // ar_check_noalloc's device-resident scratch on this device; a
+        // failure here only disables that entry point
+        DeviceGuard g(device);
+        const hipError_t e = g.ok ? arlib::check_static_scratch(device, &c->check_static)
+                                  : hipErrorInvalidDevice;
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            c->check_static = nullptr;
+            c->check_static_error = hipGetErrorString(e);
+        }
+    }
     *out = c;
     return AR_OK;
 }
@@ -839,8 +855,14 @@ ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* 
     }
 }
 
-ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
-                   const double* ref, const double* bound, ar_check_result* result) {
+namespace {
+
+// ar_check and ar_check_noalloc: the same validation and kernels; the
+// partial records go to the context's allocated array or to the
+// device-resident one.
+ar_status check_impl(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
+                     const double* ref, const double* bound, ar_check_result* result,
+                     bool noalloc) {
     if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
     try {
         if (!result) return fail(ctx, AR_ERR_INVALID_ARG, "result is NULL");
@@ -867,7 +889,13 @@ ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_
         }
         DeviceGuard g(ctx->device);
         if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
-        if (!ctx->check_part) {
+        if (noalloc && !ctx->check_static)
+            return fail(ctx, AR_ERR_RUNTIME, "the device-resident scratch is unavailable: %s",
+                        ctx->check_static_error.c_str());
+        if (noalloc && arlib::check_blocks(count) > arlib::kCheckMaxBlocks)
+            return fail(ctx, AR_ERR_INVALID_ARG, "count %zu needs more than %u partial records",
+                        count, arlib::kCheckMaxBlocks);   // unreachable: the grid is capped
+        if (!noalloc && !ctx->check_part) {
             void* p = nullptr;
             if (hipMalloc(&p, sizeof(arlib::CheckPartial) * arlib::kCheckMaxBlocks) != hipSuccess ||
                 !p) {
@@ -884,7 +912,8 @@ ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_
         a.eb = (int)elem_bytes(dtype);
         a.ref = count ? ref : nullptr;
         a.bound = count ? bound : nullptr;
-        const hipError_t e = arlib::launch_check(a, ctx->check_part, result, ctx->stream);
+        const hipError_t e = arlib::launch_check(
+            a, noalloc ? ctx->check_static : ctx->check_part, result, ctx->stream);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(ctx, AR_ERR_RUNTIME, "check launch failed: %s", hipGetErrorString(e));
@@ -895,6 +924,19 @@ ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_
     } catch (...) {
         return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
     }
+}
+
+}  // namespace
+
+ar_status ar_check(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
+                   const double* ref, const double* bound, ar_check_result* result) {
+    return check_impl(ctx, bufs, nranks, count, dtype, ref, bound, result, false);
+}
+
+ar_status ar_check_noalloc(ar_ctx* ctx, void* const* bufs, int nranks, size_t count,
+                           ar_dtype dtype, const double* ref, const double* bound,
+                           ar_check_result* result) {
+    return check_impl(ctx, bufs, nranks, count, dtype, ref, bound, result, true);
 }
 
 const char* ar_status_string(ar_status s) {

@@ -15,9 +15,17 @@
 //     and writes the result.
 // Two passes and a fixed combination tree make the result deterministic and
 // need no atomics.
+#include <mutex>
+
 #include "common.h"
 
 namespace arlib {
+
+// The scratch of ar_check_noalloc: kCheckMaxBlocks partial records resident
+// on every GPU the library runs on, for the life of the process.  Host code
+// uses the per-device address from check_static_scratch(), never this name
+// (on the host it only stands in for the symbol).
+static __device__ __align__(256) CheckPartial scratch[kCheckMaxBlocks];
 
 namespace {
 
@@ -140,6 +148,27 @@ __global__ __launch_bounds__(kCheckThreads) void k_check_final(const CheckPartia
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+CheckPartial* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t check_static_scratch(int device, CheckPartial** out) {
+    *out = nullptr;
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = static_cast<CheckPartial*>(p);
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
 
 unsigned check_blocks(size_t count) {
     const size_t want = ceil_div(count, (size_t)kCheckThreads);

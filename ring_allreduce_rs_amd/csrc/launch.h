@@ -81,7 +81,7 @@ hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int
 // On-device result checker (check.hip): pass 1 writes one partial record per
 // block (at most kCheckMaxBlocks) to `part`, pass 2 folds them into `out`.
 constexpr int kCheckThreads = 256;
-constexpr unsigned kCheckMaxBlocks = 2048;
+constexpr unsigned kCheckMaxBlocks = AR_CHECK_MAX_RECORDS;
 struct CheckArgs {
     RankTable t;
     size_t count;
@@ -100,6 +100,9 @@ struct CheckPartial {
     unsigned pad;
 };
 unsigned check_blocks(size_t count);   // blocks of pass 1 (partial records written)
+// The device address of the device-resident scratch (kCheckMaxBlocks
+// records) on `device`, which must be current; looked up once per device.
+hipError_t check_static_scratch(int device, CheckPartial** out);
 hipError_t launch_check(const CheckArgs& a, CheckPartial* part, ar_check_result* out,
                         hipStream_t s);
 

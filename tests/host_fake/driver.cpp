@@ -496,6 +496,16 @@ void check_checker(ar_ctx* ctx) {
     CHECK(fc.kernel_launches == l0 + 4 && fc.device_allocs == a0 + 1, "scratch kept");
     CHECK(ar_check(ctx, bufs, 3, 0, AR_INT32, nullptr, nullptr, res) == AR_OK, "check count 0");
     CHECK(fc.kernel_launches == l0 + 5, "count 0: the final pass only");
+    // the allocation-free variant: same validation, no allocation
+    bad(ar_check_noalloc(ctx, bufs, 8, 100, AR_FLOAT32, nullptr, bound, res), "noalloc bound");
+    bad(ar_check_noalloc(ctx, bufs, 8, 100, AR_FLOAT32, nullptr, nullptr, nullptr), "noalloc NULL");
+    CHECK(fc.kernel_launches == l0 + 5, "a rejected noalloc check launched");
+    CHECK(ar_check_noalloc(ctx, bufs, 8, (size_t)1 << 33, AR_FLOAT32, nullptr, nullptr, res) ==
+              AR_OK, "noalloc check");
+    CHECK(ar_check_noalloc(ctx, bufs, 2, 5, AR_BFLOAT16, ref, bound, res) == AR_OK, "noalloc 2");
+    CHECK(fc.kernel_launches == l0 + 9 && fc.device_allocs == a0 + 1, "noalloc allocated");
+    CHECK(ar_check_noalloc(nullptr, bufs, 2, 5, AR_INT32, nullptr, nullptr, res) ==
+              AR_ERR_INVALID_ARG, "noalloc NULL ctx");
 }
 
 int main() {
