@@ -158,23 +158,31 @@ def copy_ceiling(ar, nbytes, reps=50):
     return 2 * nb / (ms * 1e-3) / 1e9, ms
 
 
-def launch_stats(ar, sets, w, algo, reps):
-    """Per-launch HIP-event times (ms) of `reps` launches rotating over the
-    bucket sets, each launch bracketed by its own pair of events on the launch
-    stream: (median, min, mean)."""
+LAUNCH_GROUP = 10               # launches between two events of the per-launch pass
+
+
+def launch_stats(ar, sets, w, algo, groups):
+    """Per-launch HIP-event times (ms): `groups` groups of LAUNCH_GROUP
+    back-to-back launches rotating over the bucket sets, one event on the
+    launch stream between consecutive groups; each group's time / LAUNCH_GROUP
+    is one sample.  (A timing event after every single launch costs a few
+    microseconds of its own, more than the spread being measured.)  Returns
+    (median, min, mean) over the groups."""
     import statistics
 
     import torch
     calls = [ar.bind(ts, op=w.op, algo=algo) for ts in sets]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        calls[i % len(calls)]()
-        b.record()
+    evs[0].record()
+    i = 0
+    for g in range(groups):
+        for _ in range(LAUNCH_GROUP):
+            calls[i % len(calls)]()
+            i += 1
+        evs[g + 1].record()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
+    ms = [evs[g].elapsed_time(evs[g + 1]) / LAUNCH_GROUP for g in range(groups)]
     return statistics.median(ms), min(ms), sum(ms) / len(ms)
 
 
@@ -512,8 +520,8 @@ def main():
     alg_bytes = 2 * w.nranks * w.bytes_per_rank
     value = alg_bytes * args.steps / wall / 1e9
     t_step = wall / args.steps
-    stat_reps = max(20, min(args.steps, 200))
-    med, mn, _ = launch_stats(ar, sets, w, args.algo, stat_reps)
+    stat_groups = max(5, min(args.steps // LAUNCH_GROUP, 40))
+    med, mn, _ = launch_stats(ar, sets, w, args.algo, stat_groups)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     key = f"{w.name}/{args.algo}"
     traffic = measured_traffic(key)
@@ -555,8 +563,9 @@ def main():
             "us_per_launch_median": round(med * 1e3, 3),
             "us_per_launch_min": round(mn * 1e3, 3),
             "frac_median": round(alg_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "per_launch_pass": (f"{stat_reps} launches over the same bucket sets, each between "
-                                "its own two HIP events, after the timed region"),
+            "per_launch_pass": (f"{stat_groups} groups of {LAUNCH_GROUP} launches over the same "
+                                "bucket sets after the timed region, one HIP event between "
+                                "groups; median and min over the groups of time / launches"),
             "algorithmic_bytes_per_launch": alg_bytes,
         },
         "gpu": torch.cuda.get_device_properties(0).name,

@@ -118,6 +118,11 @@ def test_ddp_bucket_config_full_oracle():
         got = to_np(ts[0])
         assert_bits_equal(got, want, algo)
         assert (np.abs(got.astype(np.float64) - f64) <= bound + 2.0 ** -149).all()
+        # the same two facts from the on-device checker
+        r = ar.check(ts, ref=torch.from_numpy(f64).cuda(),
+                     bound=torch.from_numpy(bound + 2.0 ** -149).cuda())
+        assert r["mismatched"] == 0 and r["over_bound"] == 0, r
+        assert r["max_abs_err"] == float(np.abs(got.astype(np.float64) - f64).max())
     tw = oracle.simulate_tree_allreduce(xs, "float32", "avg").state[0]
     hw = oracle.simulate_hd_allreduce(xs, "float32", "avg").state[0]
     for algo, want in (("tree", tw), ("tree_fused", tw), ("halving_doubling", hw),
@@ -151,6 +156,7 @@ def test_bf16_2gib_config():
     for r in range(w.nranks):
         assert torch.equal(a[r], b[r]), f"fused != step on rank {r}"
     assert ranks_identical(a)
+    assert ar.check(b)["mismatched"] == 0
     want = oracle.ring_fold_at(vals, chunk_ids(idx, w.count, w.nranks), w.nranks, "bfloat16", "sum")
     assert_bits_equal(gather(a[:1], idx)[0], want, "sampled positions")
     # bf16 bound: (N-1) hops of an fp32 add then a bf16 rounding
@@ -257,6 +263,7 @@ def test_ragged_config(w):
     for r in range(w.nranks):
         assert torch.equal(a[r], ref), f"rank {r} differs from the whole-array reference"
         assert torch.equal(b[r], ref), f"ring_step rank {r} differs"
+    assert ar.check(a)["mismatched"] == 0
     want = (oracle.exact_max(vals, w.dtype) if w.op == "max" else oracle.exact_int_sum(vals))
     assert_bits_equal(gather(a[:1], idx)[0], want, "sampled positions")
     del b, ref
