@@ -36,10 +36,11 @@
  *    element.  On the 16-byte path, chunks whose bodies start off a 128-byte
  *    line of bufs[0] have their tiles shifted onto lines, so they move no
  *    more bytes than aligned ones.
- *  - The device-memory check of bufs (device, type, extent inside the
- *    allocation) is cached per context for the 32 most recent pointer sets;
- *    a buffer freed and re-allocated smaller at the same address between two
- *    calls is not re-checked.
+ *  - Every call checks that each buffer is device memory of the context's
+ *    device and that `count` elements lie inside its allocation (the runtime
+ *    reports an allocation's extent; a sub-allocation of a caching allocator
+ *    is checked against the whole segment).  ar_set_pointer_cache can trade
+ *    that per-call check for a cache of recently checked pointer sets.
  */
 #ifndef RING_ALLREDUCE_AR_H
 #define RING_ALLREDUCE_AR_H
@@ -189,6 +190,15 @@ ar_status ar_set_stream(ar_ctx* ctx, void* stream);
 #define AR_GRAPHS_MAX_BYTES_DEFAULT ((size_t)8 << 20)
 ar_status ar_set_graphs(ar_ctx* ctx, size_t max_bytes_per_rank);
 
+/* Pointer-set cache (off by default).  enable != 0: the device-memory check
+ * of bufs is remembered for the 32 most recent pointer sets and skipped when
+ * the same set comes back with at most the byte size it was checked for --
+ * for callers that reduce the same buckets every step and can guarantee that
+ * a buffer is never freed and re-allocated smaller at the same address while
+ * it is in use (that case would not be re-checked).  enable == 0 clears the
+ * cache and checks every call.  Errors: ctx == NULL -> AR_ERR_INVALID_ARG. */
+ar_status ar_set_pointer_cache(ar_ctx* ctx, int enable);
+
 /* AllReduce in place: every bufs[r][0:count) ends with the reduction of all
  * ranks' inputs.  RING_STEP and RING_FUSED give identical bits; TREE and
  * HALVING_DOUBLING give their tree-order results. */
@@ -292,7 +302,8 @@ ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes);
  * src and dst are HOST arrays of DEVICE pointers (read during the call),
  * every buffer 16-byte aligned, device memory of the context's device, no two
  * overlapping, except that dst[i] may equal src[i] (in place, as an
- * AllReduce works); bytes a multiple of 16; 1 <= nsrc + ndst <= AR_MAX_RANKS.
+ * AllReduce works); bytes a multiple of 16; nsrc and ndst at most
+ * AR_MAX_RANKS each, not both 0, and at most AR_MAX_RANKS distinct buffers.
  * Enqueued on the context's stream.  Errors: AR_ERR_INVALID_ARG for any of
  * the above, AR_ERR_RUNTIME if the launch fails. */
 ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* dst, int ndst,

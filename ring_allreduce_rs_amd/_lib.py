@@ -30,11 +30,11 @@ ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 # every symbol include/ar.h declares
 EXPORTS = (
-    "ar_create", "ar_set_stream", "ar_set_graphs", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
-    "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step", "ar_hd_rs_step", "ar_hd_ag_step",
-    "ar_dtree_step",
-    "ar_chunk_range", "ar_predict_us", "ar_auto_algo", "ar_copy", "ar_stream", "ar_check", "ar_check_noalloc",
-    "ar_status_string", "ar_last_error", "ar_destroy",
+    "ar_create", "ar_set_stream", "ar_set_graphs", "ar_set_pointer_cache", "ar_allreduce",
+    "ar_reduce_scatter", "ar_allgather", "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step",
+    "ar_hd_rs_step", "ar_hd_ag_step", "ar_dtree_step", "ar_chunk_range", "ar_predict_us",
+    "ar_auto_algo", "ar_copy", "ar_stream", "ar_check", "ar_check_noalloc", "ar_status_string",
+    "ar_last_error", "ar_destroy",
 )
 
 
@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "ar_create": ([ctypes.POINTER(vp), i, vp], i),
         "ar_set_stream": ([vp, vp], i),
         "ar_set_graphs": ([vp, sz], i),
+        "ar_set_pointer_cache": ([vp, i], i),
         "ar_allreduce": ([vp, pp, i, sz, i, i, i], i),
         "ar_reduce_scatter": ([vp, pp, i, sz, i, i, i], i),
         "ar_allgather": ([vp, pp, i, sz, i, i], i),
@@ -139,6 +140,10 @@ class Context:
         self._h = h
         self.device = device
         self._stream = stream or 0
+        # the torch wrappers derive every count from the tensors themselves,
+        # so a cached pointer set can never be used with more bytes than its
+        # allocations now hold
+        self._check(lib.ar_set_pointer_cache(self._h, 1), "ar_set_pointer_cache")
 
     @property
     def handle(self):

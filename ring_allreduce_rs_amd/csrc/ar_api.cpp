@@ -49,6 +49,9 @@ struct ar_ctx {
     // Recently validated pointer sets (least recently used is replaced): a
     // training loop reduces the same few buckets every step, and checking 64
     // pointers with the runtime costs more than a small message's kernel.
+    // Off unless the caller turns it on (ar_set_pointer_cache): a buffer freed
+    // and re-allocated smaller at the same address would not be re-checked.
+    bool ptr_cache = false;
     std::vector<CheckedSet> checked;
     uint64_t clock = 0;
     // Graph replay of multi-launch collectives (ar_set_graphs): one
@@ -244,8 +247,10 @@ ar_status check_buffers(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
     *mis = *vec ? m0 : 0;
 
     // Device-memory checks: every buffer must be device memory of ctx->device
-    // and lie inside its allocation.  Passing sets are cached (see ar_ctx).
+    // and lie inside its allocation.  With the pointer cache on, passing sets
+    // are remembered (see ar_ctx).
     for (CheckedSet& cs : ctx->checked) {
+        if (!ctx->ptr_cache) break;
         if (cs.ptrs.size() != (size_t)nranks || bytes > cs.bytes) continue;
         bool same = true;
         for (int r = 0; same && r < nranks; ++r)
@@ -281,6 +286,7 @@ ar_status check_buffers(ar_ctx* ctx, void* const* bufs, int nranks, size_t count
             return fail(ctx, AR_ERR_INVALID_ARG,
                         "bufs[%d]: %zu bytes run past the end of its allocation", r, bytes);
     }
+    if (!ctx->ptr_cache) return AR_OK;
     CheckedSet entry;
     entry.ptrs.resize((size_t)nranks);
     for (int r = 0; r < nranks; ++r) entry.ptrs[(size_t)r] = reinterpret_cast<uintptr_t>(bufs[r]);
@@ -715,6 +721,13 @@ ar_status ar_set_graphs(ar_ctx* ctx, size_t max_bytes_per_rank) {
     return AR_OK;
 }
 
+ar_status ar_set_pointer_cache(ar_ctx* ctx, int enable) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->ptr_cache = enable != 0;
+    if (!ctx->ptr_cache) ctx->checked.clear();
+    return AR_OK;
+}
+
 ar_status ar_allreduce(ar_ctx* ctx, void* const* bufs, int nranks, size_t count, ar_dtype dtype,
                        ar_op op, ar_algo algo) {
     return collective(ctx, COLL_AR, bufs, nranks, count, (int)dtype, (int)op, (int)algo);
@@ -817,9 +830,10 @@ ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* 
                     size_t bytes) {
     if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
     try {
-        if (nsrc < 0 || ndst < 0 || nsrc + ndst < 1 || nsrc + ndst > AR_MAX_RANKS)
-            return fail(ctx, AR_ERR_INVALID_ARG, "nsrc %d + ndst %d outside [1, %d]", nsrc, ndst,
-                        AR_MAX_RANKS);
+        if (nsrc < 0 || ndst < 0 || nsrc > AR_MAX_RANKS || ndst > AR_MAX_RANKS ||
+            nsrc + ndst < 1)
+            return fail(ctx, AR_ERR_INVALID_ARG, "nsrc %d / ndst %d outside [0, %d], or both 0",
+                        nsrc, ndst, AR_MAX_RANKS);
         if ((nsrc && !src) || (ndst && !dst)) return fail(ctx, AR_ERR_INVALID_ARG, "NULL array");
         if (bytes % 16) return fail(ctx, AR_ERR_INVALID_ARG, "bytes %zu is not a multiple of 16",
                                     bytes);
@@ -832,6 +846,9 @@ ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* 
         for (int i = 0; i < nsrc; ++i) all.push_back(const_cast<void*>(src[i]));
         for (int i = 0; i < ndst; ++i)
             if (!(i < nsrc && dst[i] == src[i])) all.push_back(dst[i]);
+        if (all.size() > (size_t)AR_MAX_RANKS)
+            return fail(ctx, AR_ERR_INVALID_ARG, "%zu distinct buffers, at most %d", all.size(),
+                        AR_MAX_RANKS);
         for (size_t i = 0; i < all.size(); ++i)
             if (reinterpret_cast<uintptr_t>(all[i]) & 15u)
                 return fail(ctx, AR_ERR_INVALID_ARG, "buffer %zu is not 16-byte aligned", i);

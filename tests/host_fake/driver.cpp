@@ -508,11 +508,48 @@ void check_checker(ar_ctx* ctx) {
               AR_ERR_INVALID_ARG, "noalloc NULL ctx");
 }
 
-int main() {
+void register_all() {
     // rank buffers of device 0, one range on device 1, the checker's arrays
     for (int r = 0; r < kMaxN; ++r) fake_register(rank_addr(r, 0), kStride, 0);
     fake_register(reinterpret_cast<void*>(kBase - kStride), kStride, 1);
     fake_register(reinterpret_cast<void*>(kAux), kStride, 0);
+}
+
+// ------------------------------------------------------- pointer cache
+// A buffer freed and re-allocated smaller at the same address: rejected on
+// the next call unless the caller turned the pointer-set cache on.
+void check_pointer_cache() {
+    const uintptr_t a = kBase - 3 * kStride, b = a + 8192;
+    void* bufs[2] = {reinterpret_cast<void*>(a), reinterpret_cast<void*>(b)};
+    auto shrink_to = [&](size_t size) {
+        fake_reset_ranges();
+        register_all();
+        fake_register(bufs[0], size, 0);
+        fake_register(bufs[1], size, 0);
+    };
+    for (int cache = 0; cache <= 1; ++cache) {
+        ar_ctx* c = nullptr;
+        CHECK(ar_create(&c, 0, nullptr) == AR_OK, "create");
+        CHECK(ar_set_pointer_cache(c, cache) == AR_OK, "set pointer cache");
+        shrink_to(4096);
+        CHECK(ar_allreduce(c, bufs, 2, 1024, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED) == AR_OK,
+              "4 KiB buffers, 4 KiB call");
+        shrink_to(2048);
+        const ar_status st = ar_allreduce(c, bufs, 2, 1024, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED);
+        if (cache) CHECK(st == AR_OK, "cache on: the documented stale-size case is not re-checked");
+        else CHECK(st == AR_ERR_INVALID_ARG, "cache off: re-allocated smaller buffers rejected");
+        CHECK(ar_set_pointer_cache(c, 0) == AR_OK, "cache off again");
+        CHECK(ar_allreduce(c, bufs, 2, 1024, AR_FLOAT32, AR_SUM, AR_ALGO_RING_FUSED) ==
+                  AR_ERR_INVALID_ARG, "turning the cache off clears it");
+        CHECK(ar_destroy(c) == AR_OK, "destroy");
+    }
+    CHECK(ar_set_pointer_cache(nullptr, 1) == AR_ERR_INVALID_ARG, "NULL ctx");
+    fake_reset_ranges();
+    register_all();
+}
+
+int main() {
+    register_all();
 
     check_chunk_range();
     check_cost_model();
@@ -531,6 +568,7 @@ int main() {
         check_launches(ctx);
         check_graphs(ctx);
         check_checker(ctx);
+        check_pointer_cache();
         // leave a few graphs recorded: ar_destroy must release them
         CHECK(ar_set_graphs(ctx, SIZE_MAX) == AR_OK, "graphs on");
         void* bufs[kMaxN];

@@ -200,7 +200,8 @@ def test_calibration_stream_rejects_bad_arguments(ctx):
     pa, pb = a.data_ptr(), b.data_ptr()
     cases = {
         "nothing": lambda: ctx.stream_ptrs([], [], 4096),
-        "65 buffers": lambda: ctx.stream_ptrs([pa] * 33, [pb] * 32, 16),
+        "65 sources": lambda: ctx.stream_ptrs([pa] * 65, [], 16),
+        "65 distinct buffers": lambda: ctx.stream_ptrs([pa] * 33, [pb] * 32, 16),
         "bytes not a multiple of 16": lambda: ctx.stream_ptrs([pa], [pb], 4000 + 8),
         "misaligned": lambda: ctx.stream_ptrs([pa + 4], [pb], 1024),
         "overlap": lambda: ctx.stream_ptrs([pa], [pa + 16], 1024),
