@@ -29,6 +29,17 @@ struct FusedDeep {
     static constexpr int B = 32;
     static constexpr bool kWrapLoads = false;
 };
+// PACED: WIDE's 8-rank batches with one unit per lane (8 KiB of loads per
+// wave per batch instead of 32), launched with an LDS reservation that caps
+// the waves resident on a CU (fused_waves_per_cu).  On calls that stream far
+// more than one round of waves, fewer and smaller requests in flight keep
+// HBM busier than the WIDE shape's 12 waves x 32 KiB per CU; on smaller
+// calls WIDE's all-at-once issue wins (measurements at fused_variant).
+struct FusedPaced {
+    static constexpr int U = 1;
+    static constexpr int B = kBatch;
+    static constexpr bool kWrapLoads = false;
+};
 // TINY: element-wise units with every rank's load in flight at once (one
 // memory round trip for up to 64 ranks instead of DEEP's two); for chunks so
 // small that latency, not bandwidth, sets the time.
@@ -37,7 +48,15 @@ struct FusedTiny {
     static constexpr int B = AR_MAX_RANKS;
     static constexpr bool kWrapLoads = true;
 };
-enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_TINY = 2 };
+enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_TINY = 2, CFG_PACED = 3 };
+// Residency caps apply to calls that touch more than these many bytes over
+// all ranks (N x bytes per rank): PACED replaces WIDE above the first, and
+// DEEP is capped above the second.
+constexpr size_t kPacedMinBytes = size_t(128) << 20;
+constexpr size_t kDeepCapMinBytes = size_t(256) << 20;
+// LDS per CU on gfx950: a block that reserves a little over 1/(W+1) of it
+// leaves room for at most W such blocks (one wave each) on the CU.
+constexpr unsigned kLdsBytesPerCU = 160u << 10;
 constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
 constexpr size_t kLeadUnits = 7;    // most idle 16-byte units before a chunk body (128-byte lines)
 // Streaming (non-temporal) loads and stores.  The fused kernel touches every
@@ -141,6 +160,10 @@ inline size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 // Which fused shape (CFG_*) a plan runs (host side; dispatch.hip).
 int fused_variant(const Plan& p);
 int fused_units_per_lane(int cfg);
+// Waves of a fused launch allowed per CU (0: no cap), and the dynamic LDS
+// bytes per block that enforce it (0: none).
+unsigned fused_waves_per_cu(const Plan& p);
+unsigned fused_lds_reserve(const Plan& p);
 
 // Launchers, one per translation unit.
 hipError_t launch_fused_kind(const Plan& p, const Args& a, dim3 grid, hipStream_t s);

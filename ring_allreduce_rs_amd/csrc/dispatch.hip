@@ -24,17 +24,72 @@ int fused_variant(const Plan& p) {
     if (p.nranks > FusedDeep::B && per <= kTinyMaxChunkBytes && p.order != ORDER_DTREE)
         return CFG_TINY;
     if (p.dtype == AR_BFLOAT16 || p.nranks > 16) return CFG_DEEP;
+    // From 8 ranks up, calls over kPacedMinBytes in all take PACED (WIDE's
+    // batches at one unit per lane, residency capped).  Measured on MI355X,
+    // fp32 SUM, cold inputs, WIDE -> PACED: 8 x 25 MiB 75.3 -> 69.7 us,
+    // 8 x 200 MiB 631 -> 540 us, 16 x 64 MiB 422 -> 342 us, 16 x 1 GiB int32
+    // 6.38 -> 5.58 ms, 10 x 64 MiB AVG 246 -> 226 us; at 8 x 16 MiB (128 MiB
+    // in all) WIDE still wins, 47.6 vs 49.1 us, and by 17-30 % at 8 x 4-8 MiB.
+    // Below 8 ranks a wave's batch is only N KiB; there PACED lost at every
+    // cap (2 x 100 MiB: 67.8 us uncapped, 85 us at best capped; 4 x 25 MiB
+    // WIDE 36.1 us vs 37.5 us).
+    const size_t total = p.count * (size_t)elem_bytes(p.dtype) * (size_t)p.nranks;
+    const int wide = p.vec && p.nranks >= kBatch && total > kPacedMinBytes ? CFG_PACED : CFG_WIDE;
     // the tree orders have a WIDE kernel for 8 ranks only (a wider one would
     // need a deeper stack of subtree results in registers)
-    if (p.order != ORDER_RING) return p.nranks == 8 && p.vec ? CFG_WIDE : CFG_DEEP;
-    if (p.nranks <= kBatch) return CFG_WIDE;
-    return per <= kDeepMaxChunkBytes ? CFG_DEEP : CFG_WIDE;
+    if (p.order != ORDER_RING) return p.nranks == 8 && p.vec ? wide : CFG_DEEP;
+    if (p.nranks <= kBatch) return wide;
+    return per <= kDeepMaxChunkBytes ? CFG_DEEP : wide;
 }
 
 int fused_units_per_lane(int cfg) {
-    return cfg == CFG_DEEP   ? FusedDeep::U
-           : cfg == CFG_TINY ? FusedTiny::U
-                             : FusedWide::U;
+    return cfg == CFG_DEEP    ? FusedDeep::U
+           : cfg == CFG_TINY  ? FusedTiny::U
+           : cfg == CFG_PACED ? FusedPaced::U
+                              : FusedWide::U;
+}
+
+unsigned fused_waves_per_cu(const Plan& p) {
+    if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return 0;
+    const int cfg = fused_variant(p);
+    // Each cap is the best of a sweep over 3-16 waves per CU, measured on
+    // MI355X with cold inputs (fp32 unless named):
+    if (cfg == CFG_PACED) {
+        // ReduceScatter (N reads, one write): 8 x 25 MiB 39.8 -> 38.6 us,
+        // 16 x 256 MiB int32 787 -> 720 us
+        if (p.kind == KIND_FUSED_RS) return 10;
+        // the pairwise orders: 8 x 25 MiB 77.8 -> 71.9 us (PAIR), 77.3 ->
+        // 71.2 us (PAIR_BITREV)
+        if (p.order == ORDER_PAIR || p.order == ORDER_PAIR_BITREV) return 7;
+        // MAX, whose fold costs more ALU: 8 x 25 MiB 68.0 us at 6 waves
+        // (69.5 at 7, 71.8 at 5), 16 x 1 GiB 5.63 ms at 6 (6.69 at 4)
+        if (p.op == AR_MAX) return 6;
+        // ring and double-tree SUM / AVG: 8 x 25 MiB 69.7 us at 5 (70.7 at 4
+        // and 6), 12 x 64 MiB 261 us at 5, 16 x 64 MiB 342 us at 4-5
+        return 5;
+    }
+    if (cfg == CFG_DEEP && p.kind == KIND_FUSED_AR) {
+        // DEEP keeps 32 ranks of loads in flight (32 KiB per wave); bf16's
+        // per-hop rounding wants more waves.  Small calls lose under any cap
+        // (64 x 4 MiB: 107.9 us uncapped, 111.6 at best).  Measured:
+        // 64 x 8 MiB 230.5 -> 202.5 us (3 waves), 64 x 64 MiB 1572 ->
+        // 1490 us (3), 32 x 32 MiB 403 -> 350 us (3), bf16 32 x 32 MiB 410 ->
+        // 366 us (4; 3 gave 408), bf16 8 x 256 MiB 703 -> 696 us (7),
+        // bf16 16 x 128 MiB 742 -> 703 us (7).
+        const size_t total = p.count * (size_t)elem_bytes(p.dtype) * (size_t)p.nranks;
+        if (total <= kDeepCapMinBytes) return 0;
+        if (p.nranks > 16) return p.dtype == AR_BFLOAT16 ? 4 : 3;
+        return p.dtype == AR_BFLOAT16 ? 7 : 0;
+    }
+    return 0;
+}
+
+unsigned fused_lds_reserve(const Plan& p) {
+    const unsigned w = fused_waves_per_cu(p);
+    if (w == 0) return 0;
+    // kLdsBytesPerCU / (w + 1/2), rounded down to 256 bytes: w blocks fit,
+    // w + 1 do not, with about half a block's share of slack either way
+    return (2u * kLdsBytesPerCU / (2u * w + 1u)) & ~255u;
 }
 
 bool plan_shape(const Plan& p, Shape* out) {

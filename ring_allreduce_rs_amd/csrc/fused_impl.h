@@ -191,7 +191,13 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
         if constexpr (ORDER == ORDER_RING) {
         // ring order: start = c+1, then c+2, ..., ending with c itself
         int r = start;
-#pragma unroll
+        // With a run-time rank count and one unit per lane the batch loop
+        // stays rolled: unrolled, the compiler hoisted later batches' loads
+        // over the adds of the fp32 SUM kernel (228 VGPRs, one wave per SIMD,
+        // 16 x 64 MiB 637 us against 342 us rolled).
+        constexpr int kOuter =
+            NR > 0 ? (NR + kB - 1) / kB : U > 1 ? (AR_MAX_RANKS + kB - 1) / kB : 1;
+#pragma unroll kOuter
         for (int j0 = 0; j0 < (NR > 0 ? NR : AR_MAX_RANKS); j0 += kB) {
             if (NR == 0 && j0 >= n) break;
             T v[kB][U];
@@ -302,7 +308,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
 // WIDE shapes, and 3.7 % slower on the 8-rank WIDE kernel, which therefore
 // keeps the plain indexing when the layout allows it.
 inline bool use_lead(const Plan& p) {
-    const bool n8_wide = p.nranks == 8 && fused_variant(p) == CFG_WIDE;
+    const int cfg = fused_variant(p);
+    const bool n8_wide = p.nranks == 8 && (cfg == CFG_WIDE || cfg == CFG_PACED);
     return p.vec && (p.lead || !n8_wide);
 }
 
@@ -311,24 +318,50 @@ inline hipError_t launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStr
     const dim3 block(kFusedThreads);
     const int cfg = fused_variant(p);
     const bool n8 = VEC && p.nranks == 8;
+    // dynamic LDS that no kernel touches: it only caps the waves per CU
+    const unsigned lds = fused_lds_reserve(p);
+    // PACED runs the 16-byte path of fp32 / int32 only (bf16 folds take DEEP)
+    constexpr bool kPaced = VEC && Op::kElemBytes == 4;
     if constexpr (VEC && !LEAD) {
-        // plain 16-byte indexing: the aligned 8-rank WIDE kernel only (use_lead)
-        if (!n8 || cfg != CFG_WIDE) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedWide, ORDER>), grid, block, 0, s, a);
+        // plain 16-byte indexing: the aligned 8-rank WIDE / PACED kernels
+        // only (use_lead)
+        if (!n8) return hipErrorInvalidConfiguration;
+        if (cfg == CFG_WIDE)
+            hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedWide, ORDER>), grid, block, lds, s, a);
+        else if constexpr (kPaced) {
+            if (cfg != CFG_PACED) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedPaced, ORDER>), grid, block, lds, s, a);
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
     } else if (cfg == CFG_TINY) {
         // element-wise units whatever the alignment (the grid was sized so);
         // never planned for the double tree (fused_variant)
         if constexpr (ORDER == ORDER_DTREE) return hipErrorInvalidConfiguration;
         else
-            hipLaunchKernelGGL((k_fused<Op, MODE, false, 0, FusedTiny, ORDER>), grid, block, 0, s,
+            hipLaunchKernelGGL((k_fused<Op, MODE, false, 0, FusedTiny, ORDER>), grid, block, lds, s,
                                a);
     } else if (cfg == CFG_DEEP) {
         // the runtime-N loop measured faster than the 8-rank unrolled one here
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep, ORDER, LEAD>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep, ORDER, LEAD>), grid, block, lds, s, a);
+    } else if (cfg == CFG_PACED) {
+        if constexpr (kPaced) {
+            if (n8)
+                hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedPaced, ORDER, LEAD>), grid, block,
+                                   lds, s, a);
+            else if constexpr (ORDER == ORDER_RING)
+                hipLaunchKernelGGL((k_fused<Op, MODE, true, 0, FusedPaced, ORDER_RING, LEAD>), grid,
+                                   block, lds, s, a);
+            else
+                return hipErrorInvalidConfiguration;   // fused_variant never asks
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
     } else if (n8) {
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide, ORDER, LEAD>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide, ORDER, LEAD>), grid, block, lds, s, a);
     } else if constexpr (ORDER == ORDER_RING) {
-        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedWide, ORDER_RING, LEAD>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedWide, ORDER_RING, LEAD>), grid, block, lds,
+                           s, a);
     } else {
         return hipErrorInvalidConfiguration;   // no such kernel (fused_variant never asks)
     }

@@ -548,8 +548,68 @@ void check_pointer_cache() {
     register_all();
 }
 
+// Residency caps of the fused launches: the LDS a capped block reserves lets
+// exactly the cap's number of blocks share a CU's LDS (and never exceeds what
+// one block may take); the PACED shape appears only from 8 ranks, on the
+// 16-byte path, above its size threshold; AllGather and uncapped shapes
+// reserve nothing.
+void check_residency_caps() {
+    using namespace arlib;
+    int paced = 0, capped = 0;
+    for (int n : {2, 4, 7, 8, 9, 16, 17, 32, 64})
+        for (int dt : {AR_INT32, AR_FLOAT32, AR_BFLOAT16})
+            for (int op : {AR_SUM, AR_MAX, AR_AVG})
+                for (int kind : {KIND_FUSED_AR, KIND_FUSED_RS, KIND_FUSED_AG})
+                    for (int order : {ORDER_RING, ORDER_PAIR, ORDER_PAIR_BITREV, ORDER_DTREE})
+                        for (size_t mib : {1, 16, 64, 127, 129, 300, 4096})
+                            for (bool vec : {false, true}) {
+                                if (order != ORDER_RING && !pow2(n)) continue;
+                                Plan p{};
+                                p.kind = (Kind)kind;
+                                p.dtype = (ar_dtype)dt;
+                                p.op = (ar_op)op;
+                                p.nranks = n;
+                                p.order = order;
+                                p.vec = vec;
+                                const size_t eb = dt == AR_BFLOAT16 ? 2 : 4;
+                                // mib: MiB over all ranks
+                                p.count = (mib << 20) / eb / (size_t)n;
+                                const size_t total = p.count * eb * (size_t)n;
+                                const int cfg = fused_variant(p);
+                                const unsigned w = fused_waves_per_cu(p);
+                                const unsigned lds = fused_lds_reserve(p);
+                                if (cfg == CFG_PACED)
+                                    CHECK(n >= kBatch && vec && dt != AR_BFLOAT16 &&
+                                              total > kPacedMinBytes && kind != KIND_FUSED_AG,
+                                          "PACED n=%d dt=%d kind=%d total=%zu", n, dt, kind, total);
+                                if (kind == KIND_FUSED_AR && n >= kBatch && vec && dt != AR_BFLOAT16 &&
+                                    total > kPacedMinBytes && (cfg == CFG_WIDE))
+                                    CHECK(false, "WIDE kept above the threshold n=%d", n);
+                                if (kind == KIND_FUSED_AG || cfg == CFG_WIDE || cfg == CFG_TINY)
+                                    CHECK(w == 0 && lds == 0, "uncapped shape reserves LDS");
+                                if (cfg == CFG_PACED) {
+                                    CHECK(w >= 3, "PACED without a cap");
+                                    ++paced;
+                                }
+                                if (w == 0) {
+                                    CHECK(lds == 0, "LDS without a cap");
+                                    continue;
+                                }
+                                CHECK(lds > 0 && lds <= (64u << 10) && lds % 256 == 0,
+                                      "reservation %u", lds);
+                                CHECK(kLdsBytesPerCU / lds == w, "cap %u but %u blocks fit (lds %u)",
+                                      w, kLdsBytesPerCU / lds, lds);
+                                // slack for a coarser allocation granule: rounding
+                                // the reservation up by 1 KiB still fits w blocks
+                                CHECK(kLdsBytesPerCU / (lds + 1024) == w, "cap %u too tight", w);
+                                ++capped;
+                            }
+    CHECK(paced > 50 && capped > paced, "caps barely exercised (%d PACED, %d capped)", paced, capped);
+}
+
 int main() {
     register_all();
+    check_residency_caps();
 
     check_chunk_range();
     check_cost_model();
