@@ -295,8 +295,10 @@ ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes);
  * reduction: reads `bytes` bytes from each of the nsrc buffers src[0..nsrc)
  * and writes their bitwise XOR (zeros when nsrc == 0) to each of the ndst
  * buffers dst[0..ndst), with the fused kernel's tiling (one 64-lane wave per
- * block, 4 KiB of every buffer per block, 8 sources of loads in flight,
- * streaming loads and stores).  nsrc = ndst = N is the ceiling of an N-rank
+ * block, 8 sources of loads in flight, streaming loads and stores; 4 KiB of
+ * every buffer per block, or -- from 8 sources holding more than 128 MiB in
+ * all, like the fused AllReduce -- 1 KiB per block with the same cap on the
+ * blocks resident per compute unit).  nsrc = ndst = N is the ceiling of an N-rank
  * fused AllReduce's N*K-read / N*K-written pattern on this hardware; other
  * mixes separate the cost of read streams from that of write streams.
  * src and dst are HOST arrays of DEVICE pointers (read during the call),

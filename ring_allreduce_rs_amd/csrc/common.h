@@ -57,6 +57,15 @@ constexpr size_t kDeepCapMinBytes = size_t(256) << 20;
 // LDS per CU on gfx950: a block that reserves a little over 1/(W+1) of it
 // leaves room for at most W such blocks (one wave each) on the CU.
 constexpr unsigned kLdsBytesPerCU = 160u << 10;
+// Dynamic LDS per one-wave block that lets at most `waves` blocks share a CU:
+// kLdsBytesPerCU / (waves + 1/2), rounded down to 256 bytes (waves fit,
+// waves + 1 do not, with about half a block's share of slack either way).
+constexpr unsigned lds_for_waves(unsigned waves) {
+    return waves == 0 ? 0u : (2u * kLdsBytesPerCU / (2u * waves + 1u)) & ~255u;
+}
+// The PACED cap of the ring SUM / AVG AllReduce, which the calibration
+// stream shares.
+constexpr unsigned kPacedRingWaves = 5;
 constexpr int kTailLane = 32;       // first lane that handles a chunk's tail elements
 constexpr size_t kLeadUnits = 7;    // most idle 16-byte units before a chunk body (128-byte lines)
 // Streaming (non-temporal) loads and stores.  The fused kernel touches every

@@ -32,11 +32,12 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t str
     return hipGetLastError();
 }
 
-// R-read / W-write stream.  The tiling is the fused kernel's WIDE shape: one
-// 64-lane wave per block, 4 units of 16 bytes per lane, so block b reads the
-// same 4 KiB of every source and writes the same 4 KiB of every destination;
-// sources are loaded 8 at a time before they are combined, destinations are
-// written one after another.  The sources are combined with XOR (one bitwise
+// R-read / W-write stream.  The tiling is the fused kernel's: one 64-lane
+// wave per block, CFG::U units of 16 bytes per lane (WIDE: 4, so block b
+// reads the same 4 KiB of every source and writes the same 4 KiB of every
+// destination; PACED: 1, with the same cap on waves per CU as the fused
+// kernel); sources are loaded 8 at a time before they are combined,
+// destinations are written one after another.  The sources are combined with XOR (one bitwise
 // instruction per word and source, no rounding), which keeps every load
 // needed and makes the output checkable.  With no source the destinations
 // get zeros; with no destination the combination is kept alive in a
@@ -50,10 +51,10 @@ struct StreamArgs {
     int ndst;
 };
 
-template <int NR>
+template <int NR, class CFG>
 __global__ __launch_bounds__(kFusedThreads) void k_stream(const StreamArgs a) {
-    constexpr int U = FusedWide::U;
-    constexpr int kB = FusedWide::B;
+    constexpr int U = CFG::U;
+    constexpr int kB = CFG::B;
     constexpr int kMax = NR > 0 ? NR : AR_MAX_RANKS;
     const int ns = NR > 0 ? NR : a.nsrc;
     const int nd = NR > 0 ? NR : a.ndst;
@@ -69,7 +70,11 @@ __global__ __launch_bounds__(kFusedThreads) void k_stream(const StreamArgs a) {
     u32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
+    // (rolled for a run-time source count at one unit per lane, as in the
+    // fused kernel: unrolled, the loads of later batches were hoisted and
+    // the kernel took 226 VGPRs)
+    constexpr int kOuter = NR > 0 || U > 1 ? (kMax + kB - 1) / kB : 1;
+#pragma unroll kOuter
     for (int j0 = 0; j0 < kMax; j0 += kB) {
         if (NR == 0 && j0 >= ns) break;
         u32x4 v[kB][U];
@@ -118,12 +123,24 @@ hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int
     a.nsrc = nsrc;
     a.ndst = ndst;
     if (a.units == 0 || nsrc + ndst == 0) return hipSuccess;
-    const size_t blocks = ceil_div(a.units, (size_t)kFusedThreads * FusedWide::U);
+    // the fused kernel's choice for an AllReduce of nsrc ranks of `bytes`
+    // each: PACED (one unit per lane, capped) from 8 sources up when the
+    // sources hold more than kPacedMinBytes in all, else WIDE
+    const bool paced = nsrc >= kBatch && (size_t)nsrc * bytes > kPacedMinBytes;
+    const size_t per_block = (size_t)kFusedThreads * (paced ? FusedPaced::U : FusedWide::U);
+    const size_t blocks = ceil_div(a.units, per_block);
     if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-    if (nsrc == 8 && ndst == 8)
-        hipLaunchKernelGGL(k_stream<8>, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, a);
+    const dim3 grid((unsigned)blocks), block(kFusedThreads);
+    const unsigned lds = paced ? lds_for_waves(kPacedRingWaves) : 0u;
+    const bool n8 = nsrc == 8 && ndst == 8;
+    if (paced && n8)
+        hipLaunchKernelGGL((k_stream<8, FusedPaced>), grid, block, lds, stream, a);
+    else if (paced)
+        hipLaunchKernelGGL((k_stream<0, FusedPaced>), grid, block, lds, stream, a);
+    else if (n8)
+        hipLaunchKernelGGL((k_stream<8, FusedWide>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(k_stream<0>, dim3((unsigned)blocks), dim3(kFusedThreads), 0, stream, a);
+        hipLaunchKernelGGL((k_stream<0, FusedWide>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -65,8 +65,10 @@ unsigned fused_waves_per_cu(const Plan& p) {
         // (69.5 at 7, 71.8 at 5), 16 x 1 GiB 5.63 ms at 6 (6.69 at 4)
         if (p.op == AR_MAX) return 6;
         // ring and double-tree SUM / AVG: 8 x 25 MiB 69.7 us at 5 (70.7 at 4
-        // and 6), 12 x 64 MiB 261 us at 5, 16 x 64 MiB 342 us at 4-5
-        return 5;
+        // and 6), 12 x 64 MiB 261 us at 5, 16 x 64 MiB 342 us at 4-5.  (How
+        // the rank buffers sit in HBM moves the best cap by one: with
+        // back-to-back buffers 8 x 25 MiB ran 67.8 us at 4 and 68.9 at 5.)
+        return kPacedRingWaves;
     }
     if (cfg == CFG_DEEP && p.kind == KIND_FUSED_AR) {
         // DEEP keeps 32 ranks of loads in flight (32 KiB per wave); bf16's
@@ -84,13 +86,7 @@ unsigned fused_waves_per_cu(const Plan& p) {
     return 0;
 }
 
-unsigned fused_lds_reserve(const Plan& p) {
-    const unsigned w = fused_waves_per_cu(p);
-    if (w == 0) return 0;
-    // kLdsBytesPerCU / (w + 1/2), rounded down to 256 bytes: w blocks fit,
-    // w + 1 do not, with about half a block's share of slack either way
-    return (2u * kLdsBytesPerCU / (2u * w + 1u)) & ~255u;
-}
+unsigned fused_lds_reserve(const Plan& p) { return lds_for_waves(fused_waves_per_cu(p)); }
 
 bool plan_shape(const Plan& p, Shape* out) {
     const size_t eb = (size_t)elem_bytes(p.dtype);
