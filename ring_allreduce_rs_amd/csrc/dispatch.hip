@@ -23,6 +23,16 @@ int fused_variant(const Plan& p) {
     // scratch memory; DEEP serves it)
     if (p.nranks > FusedDeep::B && per <= kTinyMaxChunkBytes && p.order != ORDER_DTREE)
         return CFG_TINY;
+    const size_t total = p.count * (size_t)elem_bytes(p.dtype) * (size_t)p.nranks;
+    const bool big = p.vec && total > kPacedMinBytes;
+    // bf16 SUM / AVG AllReduce over 8 ranks: PACED with the 8-rank loop
+    // (8 x 2 GiB 5.40 -> 5.34 ms, 8 x 12.5 Mi elements AVG 75.9 -> 68.9 us
+    // against capped / uncapped DEEP); bf16 MAX, whose fold is the most ALU
+    // per byte here, keeps DEEP without a cap (8 x 128 Mi: 704 us, PACED at
+    // best 696 with 10 waves).
+    if (p.dtype == AR_BFLOAT16 && big && p.nranks == kBatch && p.kind == KIND_FUSED_AR &&
+        p.order == ORDER_RING && p.op != AR_MAX)
+        return CFG_PACED;
     if (p.dtype == AR_BFLOAT16 || p.nranks > 16) return CFG_DEEP;
     // From 8 ranks up, calls over kPacedMinBytes in all take PACED (WIDE's
     // batches at one unit per lane, residency capped).  Measured on MI355X,
@@ -33,8 +43,7 @@ int fused_variant(const Plan& p) {
     // Below 8 ranks a wave's batch is only N KiB; there PACED lost at every
     // cap (2 x 100 MiB: 67.8 us uncapped, 85 us at best capped; 4 x 25 MiB
     // WIDE 36.1 us vs 37.5 us).
-    const size_t total = p.count * (size_t)elem_bytes(p.dtype) * (size_t)p.nranks;
-    const int wide = p.vec && p.nranks >= kBatch && total > kPacedMinBytes ? CFG_PACED : CFG_WIDE;
+    const int wide = big && p.nranks >= kBatch ? CFG_PACED : CFG_WIDE;
     // the tree orders have a WIDE kernel for 8 ranks only (a wider one would
     // need a deeper stack of subtree results in registers)
     if (p.order != ORDER_RING) return p.nranks == 8 && p.vec ? wide : CFG_DEEP;
@@ -52,8 +61,12 @@ int fused_units_per_lane(int cfg) {
 unsigned fused_waves_per_cu(const Plan& p) {
     if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return 0;
     const int cfg = fused_variant(p);
-    // Each cap is the best of a sweep over 3-16 waves per CU, measured on
-    // MI355X with cold inputs (fp32 unless named):
+    // How many waves a CU needs depends on the bytes a wave keeps in flight
+    // and on the fold's ALU work per byte: the IEEE maximum of fp32 / bf16
+    // (NaN handling, bf16 widening) wants more waves than an add or an
+    // integer max.  Each cap is the best of a sweep over 3-16 waves per CU
+    // (or none), measured on MI355X with cold inputs (fp32 unless named):
+    const bool fmax = p.op == AR_MAX && p.dtype != AR_INT32;
     if (cfg == CFG_PACED) {
         // ReduceScatter (N reads, one write): 8 x 25 MiB 39.8 -> 38.6 us,
         // 16 x 256 MiB int32 787 -> 720 us
@@ -61,27 +74,42 @@ unsigned fused_waves_per_cu(const Plan& p) {
         // the pairwise orders: 8 x 25 MiB 77.8 -> 71.9 us (PAIR), 77.3 ->
         // 71.2 us (PAIR_BITREV)
         if (p.order == ORDER_PAIR || p.order == ORDER_PAIR_BITREV) return 7;
-        // MAX, whose fold costs more ALU: 8 x 25 MiB 68.0 us at 6 waves
-        // (69.5 at 7, 71.8 at 5), 16 x 1 GiB 5.63 ms at 6 (6.69 at 4)
-        if (p.op == AR_MAX) return 6;
-        // ring and double-tree SUM / AVG: 8 x 25 MiB 69.7 us at 5 (70.7 at 4
-        // and 6), 12 x 64 MiB 261 us at 5, 16 x 64 MiB 342 us at 4-5.  (How
-        // the rank buffers sit in HBM moves the best cap by one: with
+        // bf16 SUM / AVG: 8 x 2 GiB 5.34 ms at 6 (5.26 at 5, 5.37 at 7),
+        // 8 x 128 Mi elements 693 us at 6-7, 8 x 12.5 Mi AVG 68.9 us at 6
+        // (71.0 at 5)
+        if (p.dtype == AR_BFLOAT16) return 6;
+        // fp32 MAX: 8 x 25 MiB 68.0 us at 6 (69.5 at 7, 71.8 at 5), 16 x 1 GiB
+        // 5.63 ms at 6 (6.69 at 4)
+        if (fmax) return 6;
+        // ring and double-tree SUM / AVG, int32 MAX: 8 x 25 MiB 69.7 us at 5
+        // (70.7 at 4 and 6), 12 x 64 MiB 261 us at 5, 16 x 64 MiB 342 us at
+        // 4-5, 16 x 1 GiB int32 MAX 5.68 ms at 5 (6.20 uncapped).  (How the
+        // rank buffers sit in HBM moves the best cap by one: with
         // back-to-back buffers 8 x 25 MiB ran 67.8 us at 4 and 68.9 at 5.)
         return kPacedRingWaves;
     }
     if (cfg == CFG_DEEP && p.kind == KIND_FUSED_AR) {
-        // DEEP keeps 32 ranks of loads in flight (32 KiB per wave); bf16's
-        // per-hop rounding wants more waves.  Small calls lose under any cap
-        // (64 x 4 MiB: 107.9 us uncapped, 111.6 at best).  Measured:
-        // 64 x 8 MiB 230.5 -> 202.5 us (3 waves), 64 x 64 MiB 1572 ->
-        // 1490 us (3), 32 x 32 MiB 403 -> 350 us (3), bf16 32 x 32 MiB 410 ->
-        // 366 us (4; 3 gave 408), bf16 8 x 256 MiB 703 -> 696 us (7),
-        // bf16 16 x 128 MiB 742 -> 703 us (7).
+        // DEEP keeps up to 32 ranks of loads in flight (32 KiB per wave).
+        // Small calls lose under any cap (64 x 4 MiB: 107.9 us uncapped,
+        // 111.6 at best).  Measured, uncapped -> capped:
         const size_t total = p.count * (size_t)elem_bytes(p.dtype) * (size_t)p.nranks;
         if (total <= kDeepCapMinBytes) return 0;
-        if (p.nranks > 16) return p.dtype == AR_BFLOAT16 ? 4 : 3;
-        return p.dtype == AR_BFLOAT16 ? 7 : 0;
+        if (p.dtype == AR_BFLOAT16) {
+            // bf16 MAX: 64 x 16 MiB 476 us uncapped, 473 at 8, 626 at 4;
+            // 8 x 256 MiB 704 uncapped, 791 at 8
+            if (p.op == AR_MAX) return 0;
+            // SUM / AVG: 32 x 32 MiB 410 -> 366 us (4; 3 gave 408), 64 x
+            // 16 MiB 458 -> 411 us (4), 16 x 128 MiB 742 -> 703 us (7)
+            return p.nranks > 16 ? 4 : 7;
+        }
+        if (p.nranks <= 16) return 0;
+        // fp32 MAX: 64 x 16 MiB 459 -> 421 us (5; 515 at 3), 32 x 32 MiB
+        // 413 -> 378 us (5; 455 at 3)
+        if (fmax) return 5;
+        // fp32 SUM / AVG, int32 SUM / MAX: 64 x 8 MiB 230.5 -> 202.5 us,
+        // 64 x 64 MiB 1572 -> 1490 us, 32 x 32 MiB 403 -> 350 us, 64 x 16 MiB
+        // int32 MAX 464 -> 383 us (all at 3)
+        return 3;
     }
     return 0;
 }

@@ -320,15 +320,16 @@ inline hipError_t launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStr
     const bool n8 = VEC && p.nranks == 8;
     // dynamic LDS that no kernel touches: it only caps the waves per CU
     const unsigned lds = fused_lds_reserve(p);
-    // PACED runs the 16-byte path of fp32 / int32 only (bf16 folds take DEEP)
-    constexpr bool kPaced = VEC && Op::kElemBytes == 4;
+    // PACED runs the 16-byte path only, and bf16 only in the 8-rank form
+    constexpr bool kPaced8 = VEC;
+    constexpr bool kPacedN = VEC && Op::kElemBytes == 4;
     if constexpr (VEC && !LEAD) {
         // plain 16-byte indexing: the aligned 8-rank WIDE / PACED kernels
         // only (use_lead)
         if (!n8) return hipErrorInvalidConfiguration;
         if (cfg == CFG_WIDE)
             hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedWide, ORDER>), grid, block, lds, s, a);
-        else if constexpr (kPaced) {
+        else if constexpr (kPaced8) {
             if (cfg != CFG_PACED) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedPaced, ORDER>), grid, block, lds, s, a);
         } else {
@@ -345,17 +346,17 @@ inline hipError_t launch_fused_n(const Plan& p, const Args& a, dim3 grid, hipStr
         // the runtime-N loop measured faster than the 8-rank unrolled one here
         hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 0, FusedDeep, ORDER, LEAD>), grid, block, lds, s, a);
     } else if (cfg == CFG_PACED) {
-        if constexpr (kPaced) {
-            if (n8)
+        if (n8) {
+            if constexpr (kPaced8)
                 hipLaunchKernelGGL((k_fused<Op, MODE, true, 8, FusedPaced, ORDER, LEAD>), grid, block,
                                    lds, s, a);
-            else if constexpr (ORDER == ORDER_RING)
-                hipLaunchKernelGGL((k_fused<Op, MODE, true, 0, FusedPaced, ORDER_RING, LEAD>), grid,
-                                   block, lds, s, a);
             else
-                return hipErrorInvalidConfiguration;   // fused_variant never asks
+                return hipErrorInvalidConfiguration;
+        } else if constexpr (kPacedN && ORDER == ORDER_RING) {
+            hipLaunchKernelGGL((k_fused<Op, MODE, true, 0, FusedPaced, ORDER_RING, LEAD>), grid, block,
+                               lds, s, a);
         } else {
-            return hipErrorInvalidConfiguration;
+            return hipErrorInvalidConfiguration;   // fused_variant never asks
         }
     } else if (n8) {
         hipLaunchKernelGGL((k_fused<Op, MODE, VEC, 8, FusedWide, ORDER, LEAD>), grid, block, lds, s, a);

@@ -578,10 +578,18 @@ void check_residency_caps() {
                                 const int cfg = fused_variant(p);
                                 const unsigned w = fused_waves_per_cu(p);
                                 const unsigned lds = fused_lds_reserve(p);
+                                // bf16: only the 8-rank ring SUM / AVG AllReduce
+                                const bool bf16_ok = dt != AR_BFLOAT16 ||
+                                                     (n == kBatch && kind == KIND_FUSED_AR &&
+                                                      order == ORDER_RING && op != AR_MAX);
                                 if (cfg == CFG_PACED)
-                                    CHECK(n >= kBatch && vec && dt != AR_BFLOAT16 &&
-                                              total > kPacedMinBytes && kind != KIND_FUSED_AG,
+                                    CHECK(n >= kBatch && vec && bf16_ok && total > kPacedMinBytes &&
+                                              kind != KIND_FUSED_AG,
                                           "PACED n=%d dt=%d kind=%d total=%zu", n, dt, kind, total);
+                                if (cfg != CFG_PACED && dt == AR_BFLOAT16 && n == kBatch && vec &&
+                                    kind == KIND_FUSED_AR && order == ORDER_RING && op != AR_MAX &&
+                                    total > kPacedMinBytes)
+                                    CHECK(false, "8-rank bf16 AllReduce not PACED above the threshold");
                                 if (kind == KIND_FUSED_AR && n >= kBatch && vec && dt != AR_BFLOAT16 &&
                                     total > kPacedMinBytes && (cfg == CFG_WIDE))
                                     CHECK(false, "WIDE kept above the threshold n=%d", n);
