@@ -48,11 +48,12 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 INFINITY_CACHE_BYTES = 256 << 20
 ALWAYS_REPLAY = 1 << 62         # graph-replay threshold that covers every size measured
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-# the sources the fused kernel and the calibration copy are built from
+# the sources the fused kernel and the calibration copy are built from, and
+# the host code that picks their shape and residency cap
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_rs_amd", "csrc", f)
                   for f in ("common.h", "elem.h", "launch.h", "fused_impl.h", "fused.hip",
                             "fused_f32.hip", "fused_bf16.hip", "fused_i32.hip", "fused_f32_lead.hip",
-                            "fused_bf16_lead.hip", "fused_i32_lead.hip", "copy.hip")]
+                            "fused_bf16_lead.hip", "fused_i32_lead.hip", "copy.hip", "dispatch.hip")]
 
 
 def kernel_source_hash() -> str:
