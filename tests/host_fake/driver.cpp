@@ -264,8 +264,12 @@ void check_launches(ar_ctx* ctx) {
                              AR_ALGO_DOUBLE_TREE_FUSED};
     const ar_dtype dts[] = {AR_INT32, AR_FLOAT32, AR_BFLOAT16};
     const ar_op ops[] = {AR_SUM, AR_MAX, AR_AVG};
+    // (the 2^22 .. 2^25 counts put most rank counts over the 128 MiB and 256 MiB
+    // thresholds of the residency-capped shapes)
     const size_t special[] = {1, 2, 3, 7, 15, 16, 17, 63, 64, 65, 4095, 4096, 4097, 65536,
-                              1000003, size_t(1) << 31, (size_t(1) << 40) + 5};
+                              1000003, (size_t(1) << 22) + 3, (size_t(1) << 23) + 8,
+                              (size_t(1) << 24) + 1, (size_t(1) << 25) + 16, size_t(1) << 31,
+                              (size_t(1) << 40) + 5};
     int calls = 0;
     for (int iter = 0; iter < 4000; ++iter) {
         const int n = 1 + (int)(rng() % kMaxN);
@@ -553,6 +557,48 @@ void check_pointer_cache() {
 // one block may take); the PACED shape appears only from 8 ranks, on the
 // 16-byte path, above its size threshold; AllGather and uncapped shapes
 // reserve nothing.
+// Calls just below and just above the size thresholds of the capped shapes,
+// through the public entry points: every launch they plan passes record()'s
+// grid-coverage check, and the PACED and capped DEEP plans among them carry
+// the LDS reservation of their cap.
+void check_capped_launches(ar_ctx* ctx) {
+    using namespace arlib;
+    int paced = 0, capped = 0;
+    const ar_algo algos[] = {AR_ALGO_RING_FUSED, AR_ALGO_TREE_FUSED,
+                             AR_ALGO_HALVING_DOUBLING_FUSED, AR_ALGO_DOUBLE_TREE_FUSED};
+    for (int n : {8, 9, 12, 16, 17, 32, 64})
+        for (ar_dtype dt : {AR_INT32, AR_FLOAT32, AR_BFLOAT16})
+            for (ar_op op : {AR_SUM, AR_MAX, AR_AVG})
+                for (int coll = 0; coll < 2; ++coll)
+                    for (ar_algo algo : algos)
+                        for (size_t mib : {128, 256})
+                            for (long delta : {-17L, 3L, 4096L})
+                                for (size_t shift : {size_t(0), size_t(4)}) {
+                                    if (dt == AR_INT32 && op == AR_AVG) continue;
+                                    if (algo != AR_ALGO_RING_FUSED && !pow2(n)) continue;
+                                    if ((algo == AR_ALGO_TREE_FUSED ||
+                                         algo == AR_ALGO_DOUBLE_TREE_FUSED) && coll != 0)
+                                        continue;
+                                    const size_t eb = eb_of(dt);
+                                    const size_t count = (size_t)((long)((mib << 20) / eb / n) + delta);
+                                    void* bufs[kMaxN];
+                                    for (int r = 0; r < n; ++r) bufs[r] = rank_addr(r, shift);
+                                    fake_clear_executed();
+                                    const ar_status st = call(ctx, coll, bufs, n, count, dt, op, algo);
+                                    CHECK(st == AR_OK, "capped sweep n=%d dt=%d op=%d coll=%d algo=%d: %d",
+                                          n, (int)dt, (int)op, coll, (int)algo, (int)st);
+                                    for (const FakeLaunch& l : fake_executed()) {
+                                        const unsigned w = fused_waves_per_cu(l.plan);
+                                        paced += fused_variant(l.plan) == CFG_PACED;
+                                        capped += w > 0;
+                                        CHECK(fused_lds_reserve(l.plan) == lds_for_waves(w),
+                                              "reservation and cap disagree");
+                                    }
+                                }
+    CHECK(paced > 100 && capped > paced, "capped shapes barely planned (%d PACED, %d capped)",
+          paced, capped);
+}
+
 void check_residency_caps() {
     using namespace arlib;
     int paced = 0, capped = 0;
@@ -634,6 +680,7 @@ int main() {
     if (ctx) {
         check_validation(ctx);
         check_launches(ctx);
+        check_capped_launches(ctx);
         check_graphs(ctx);
         check_checker(ctx);
         check_pointer_cache();
