@@ -199,6 +199,19 @@ ar_status ar_set_graphs(ar_ctx* ctx, size_t max_bytes_per_rank);
  * cache and checks every call.  Errors: ctx == NULL -> AR_ERR_INVALID_ARG. */
 ar_status ar_set_pointer_cache(ar_ctx* ctx, int enable);
 
+/* Residency caps of the one-pass kernels (on by default).  Large one-pass
+ * AllReduce / ReduceScatter calls (more than 128 MiB over all ranks, from 8
+ * ranks up; DEEP shapes above 256 MiB) launch with dynamic LDS that no kernel
+ * touches, so that only 3-10 of their one-wave blocks fit on a compute unit
+ * at once: fewer, smaller memory requests per CU stream HBM faster (on
+ * MI355X, 8 x 25 MiB fp32: 70 us capped, 75 us uncapped).  While such a call
+ * runs it holds most of each CU's LDS; a caller that overlaps it with kernels
+ * needing LDS (GEMMs on another stream) can turn the caps off (enable == 0):
+ * the same calls then run the uncapped shapes and reserve no LDS.  Results
+ * are bitwise the same either way.  ar_stream follows the setting.  Errors:
+ * ctx == NULL -> AR_ERR_INVALID_ARG. */
+ar_status ar_set_residency_caps(ar_ctx* ctx, int enable);
+
 /* AllReduce in place: every bufs[r][0:count) ends with the reduction of all
  * ranks' inputs.  RING_STEP and RING_FUSED give identical bits; TREE and
  * HALVING_DOUBLING give their tree-order results. */

@@ -87,6 +87,13 @@ def set_graphs(enable: bool = True, device: int = 0,
     context(device).set_graphs(max_bytes_per_rank if enable else 0)
 
 
+def set_residency_caps(enable: bool = True, device: int = 0) -> None:
+    """Residency caps of the large one-pass calls on or off for the device's
+    context (see ar_set_residency_caps): off for callers that overlap the
+    collective with kernels needing LDS."""
+    context(device).set_residency_caps(enable)
+
+
 def allreduce(tensors, op: str = "sum", algo: str = "ring_fused"):
     """In-place AllReduce over the rank tensors; returns them."""
     ts, dt, count, dev = _check(tensors)

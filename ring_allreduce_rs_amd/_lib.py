@@ -30,7 +30,8 @@ ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 # every symbol include/ar.h declares
 EXPORTS = (
-    "ar_create", "ar_set_stream", "ar_set_graphs", "ar_set_pointer_cache", "ar_allreduce",
+    "ar_create", "ar_set_stream", "ar_set_graphs", "ar_set_pointer_cache",
+    "ar_set_residency_caps", "ar_allreduce",
     "ar_reduce_scatter", "ar_allgather", "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step",
     "ar_hd_rs_step", "ar_hd_ag_step", "ar_dtree_step", "ar_chunk_range", "ar_predict_us",
     "ar_auto_algo", "ar_copy", "ar_stream", "ar_check", "ar_check_noalloc", "ar_status_string",
@@ -68,6 +69,7 @@ def _load() -> ctypes.CDLL:
         "ar_set_stream": ([vp, vp], i),
         "ar_set_graphs": ([vp, sz], i),
         "ar_set_pointer_cache": ([vp, i], i),
+        "ar_set_residency_caps": ([vp, i], i),
         "ar_allreduce": ([vp, pp, i, sz, i, i, i], i),
         "ar_reduce_scatter": ([vp, pp, i, sz, i, i, i], i),
         "ar_allgather": ([vp, pp, i, sz, i, i], i),
@@ -159,6 +161,12 @@ class Context:
         """Replay multi-launch collectives of at most this many bytes per rank
         from recorded HIP graphs; 0 turns replay off (ar_set_graphs)."""
         self._check(lib.ar_set_graphs(self._h, max_bytes_per_rank), "ar_set_graphs")
+
+    def set_residency_caps(self, enable: bool) -> None:
+        """Residency caps of the large one-pass calls on (the default) or off
+        (ar_set_residency_caps); results are the same bits either way."""
+        self._check(lib.ar_set_residency_caps(self._h, 1 if enable else 0),
+                    "ar_set_residency_caps")
 
     def last_error(self) -> str:
         return lib.ar_last_error(self._h).decode()

@@ -53,6 +53,9 @@ struct ar_ctx {
     // and re-allocated smaller at the same address would not be re-checked.
     bool ptr_cache = false;
     std::vector<CheckedSet> checked;
+    // Residency caps of the fused kernels (ar_set_residency_caps): on unless
+    // the caller turns them off
+    bool caps = true;
     uint64_t clock = 0;
     // Graph replay of multi-launch collectives (ar_set_graphs): one
     // instantiated graph per (collective, algorithm, shape, pointer set),
@@ -391,6 +394,7 @@ struct Launch {
     bool vec;
     unsigned mis;
     arlib::RankTable t;
+    bool caps;   // residency caps allowed (the fused kinds)
 };
 
 // The kernels of L, in launch order.
@@ -407,6 +411,7 @@ std::vector<arlib::Plan> plans_of(const Launch& L) {
         const bool fused = k == arlib::KIND_FUSED_AR || k == arlib::KIND_FUSED_RS ||
                            k == arlib::KIND_FUSED_AG;
         ps.back().lead = fused && L.vec && !lines;
+        ps.back().caps = L.caps;
     };
     const arlib::Kind fused = L.coll == COLL_AR   ? arlib::KIND_FUSED_AR
                               : L.coll == COLL_RS ? arlib::KIND_FUSED_RS
@@ -485,6 +490,7 @@ std::vector<uint64_t> key_of(const Launch& L) {
     k.push_back((uint64_t)L.count);
     k.push_back((uint64_t)L.vec);
     k.push_back((uint64_t)L.mis);
+    k.push_back((uint64_t)L.caps);
     for (int r = 0; r < L.nranks; ++r) k.push_back(reinterpret_cast<uint64_t>(L.t.p[r]));
     return k;
 }
@@ -618,7 +624,7 @@ ar_status collective(ar_ctx* ctx, Coll coll, void* const* bufs, int nranks, size
                         algo, nranks);
         if (count == 0 || nranks == 1) return AR_OK;
         const Launch L{coll, algo, dtype, coll == COLL_AG ? AR_SUM : op, nranks, count, vec, mis,
-                       table_of(bufs, nranks)};
+                       table_of(bufs, nranks), ctx->caps};
         const std::vector<arlib::Plan> plans = plans_of(L);
         s = check_shapes(ctx, plans);
         if (s != AR_OK) return s;
@@ -718,6 +724,12 @@ ar_status ar_set_graphs(ar_ctx* ctx, size_t max_bytes_per_rank) {
         DeviceGuard g(ctx->device);
         clear_graphs(ctx);
     }
+    return AR_OK;
+}
+
+ar_status ar_set_residency_caps(ar_ctx* ctx, int enable) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    ctx->caps = enable != 0;
     return AR_OK;
 }
 
@@ -859,7 +871,7 @@ ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* 
         if (s != AR_OK) return s;
         DeviceGuard g(ctx->device);
         if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
-        const hipError_t e = arlib::launch_stream(src, nsrc, dst, ndst, bytes, ctx->stream);
+        const hipError_t e = arlib::launch_stream(src, nsrc, dst, ndst, bytes, ctx->caps, ctx->stream);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(ctx, AR_ERR_RUNTIME, "stream launch failed: %s", hipGetErrorString(e));

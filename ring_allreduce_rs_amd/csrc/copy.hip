@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_stream(const StreamArgs a) {
 }
 
 hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
-                         size_t bytes, hipStream_t stream) {
+                         size_t bytes, bool caps, hipStream_t stream) {
     if (nsrc < 0 || ndst < 0 || nsrc > AR_MAX_RANKS || ndst > AR_MAX_RANKS)
         return hipErrorInvalidValue;
     StreamArgs a;
@@ -126,7 +126,7 @@ hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int
     // the fused kernel's choice for an AllReduce of nsrc ranks of `bytes`
     // each: PACED (one unit per lane, capped) from 8 sources up when the
     // sources hold more than kPacedMinBytes in all, else WIDE
-    const bool paced = nsrc >= kBatch && (size_t)nsrc * bytes > kPacedMinBytes;
+    const bool paced = caps && nsrc >= kBatch && (size_t)nsrc * bytes > kPacedMinBytes;
     const size_t per_block = (size_t)kFusedThreads * (paced ? FusedPaced::U : FusedWide::U);
     const size_t blocks = ceil_div(a.units, per_block);
     if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;

@@ -30,7 +30,7 @@ int fused_variant(const Plan& p) {
     // against capped / uncapped DEEP); bf16 MAX, whose fold is the most ALU
     // per byte here, keeps DEEP without a cap (8 x 128 Mi: 704 us, PACED at
     // best 696 with 10 waves).
-    if (p.dtype == AR_BFLOAT16 && big && p.nranks == kBatch && p.kind == KIND_FUSED_AR &&
+    if (p.caps && p.dtype == AR_BFLOAT16 && big && p.nranks == kBatch && p.kind == KIND_FUSED_AR &&
         p.order == ORDER_RING && p.op != AR_MAX)
         return CFG_PACED;
     if (p.dtype == AR_BFLOAT16 || p.nranks > 16) return CFG_DEEP;
@@ -43,7 +43,7 @@ int fused_variant(const Plan& p) {
     // Below 8 ranks a wave's batch is only N KiB; there PACED lost at every
     // cap (2 x 100 MiB: 67.8 us uncapped, 85 us at best capped; 4 x 25 MiB
     // WIDE 36.1 us vs 37.5 us).
-    const int wide = big && p.nranks >= kBatch ? CFG_PACED : CFG_WIDE;
+    const int wide = p.caps && big && p.nranks >= kBatch ? CFG_PACED : CFG_WIDE;
     // the tree orders have a WIDE kernel for 8 ranks only (a wider one would
     // need a deeper stack of subtree results in registers)
     if (p.order != ORDER_RING) return p.nranks == 8 && p.vec ? wide : CFG_DEEP;
@@ -59,7 +59,7 @@ int fused_units_per_lane(int cfg) {
 }
 
 unsigned fused_waves_per_cu(const Plan& p) {
-    if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return 0;
+    if (!p.caps || (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS)) return 0;
     const int cfg = fused_variant(p);
     // How many waves a CU needs depends on the bytes a wave keeps in flight
     // and on the fold's ALU work per byte: the IEEE maximum of fp32 / bf16

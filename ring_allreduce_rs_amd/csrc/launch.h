@@ -56,6 +56,9 @@ struct Plan {
     // buffer.  The kernel then shifts its tiles back to the line (up to 7 idle
     // 16-byte units at the front) and the grid carries that slack.
     bool lead = false;
+    // Fused kinds: residency caps allowed (the PACED shape and the LDS
+    // reservations); off, large calls run the uncapped shapes
+    bool caps = true;
 };
 
 // Grid / block shape a plan launches with (for logging and tests).
@@ -74,9 +77,11 @@ hipError_t launch(const Plan& p, const RankTable& t, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 // Calibration stream: read `bytes` from each of nsrc buffers, write their XOR
-// to each of ndst buffers (16-byte aligned pointers, bytes a multiple of 16).
+// to each of ndst buffers (16-byte aligned pointers, bytes a multiple of 16),
+// in the shape the fused AllReduce of the sources would run (`caps`: residency
+// caps allowed).
 hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
-                         size_t bytes, hipStream_t stream);
+                         size_t bytes, bool caps, hipStream_t stream);
 
 // On-device result checker (check.hip): pass 1 writes one partial record per
 // block (at most kCheckMaxBlocks) to `part`, pass 2 folds them into `out`.

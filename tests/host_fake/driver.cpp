@@ -563,40 +563,49 @@ void check_pointer_cache() {
 // the LDS reservation of their cap.
 void check_capped_launches(ar_ctx* ctx) {
     using namespace arlib;
-    int paced = 0, capped = 0;
-    const ar_algo algos[] = {AR_ALGO_RING_FUSED, AR_ALGO_TREE_FUSED,
-                             AR_ALGO_HALVING_DOUBLING_FUSED, AR_ALGO_DOUBLE_TREE_FUSED};
-    for (int n : {8, 9, 12, 16, 17, 32, 64})
-        for (ar_dtype dt : {AR_INT32, AR_FLOAT32, AR_BFLOAT16})
-            for (ar_op op : {AR_SUM, AR_MAX, AR_AVG})
-                for (int coll = 0; coll < 2; ++coll)
-                    for (ar_algo algo : algos)
-                        for (size_t mib : {128, 256})
-                            for (long delta : {-17L, 3L, 4096L})
-                                for (size_t shift : {size_t(0), size_t(4)}) {
-                                    if (dt == AR_INT32 && op == AR_AVG) continue;
-                                    if (algo != AR_ALGO_RING_FUSED && !pow2(n)) continue;
-                                    if ((algo == AR_ALGO_TREE_FUSED ||
-                                         algo == AR_ALGO_DOUBLE_TREE_FUSED) && coll != 0)
-                                        continue;
-                                    const size_t eb = eb_of(dt);
-                                    const size_t count = (size_t)((long)((mib << 20) / eb / n) + delta);
-                                    void* bufs[kMaxN];
-                                    for (int r = 0; r < n; ++r) bufs[r] = rank_addr(r, shift);
-                                    fake_clear_executed();
-                                    const ar_status st = call(ctx, coll, bufs, n, count, dt, op, algo);
-                                    CHECK(st == AR_OK, "capped sweep n=%d dt=%d op=%d coll=%d algo=%d: %d",
-                                          n, (int)dt, (int)op, coll, (int)algo, (int)st);
-                                    for (const FakeLaunch& l : fake_executed()) {
-                                        const unsigned w = fused_waves_per_cu(l.plan);
-                                        paced += fused_variant(l.plan) == CFG_PACED;
-                                        capped += w > 0;
-                                        CHECK(fused_lds_reserve(l.plan) == lds_for_waves(w),
-                                              "reservation and cap disagree");
+    CHECK(ar_set_residency_caps(nullptr, 1) == AR_ERR_INVALID_ARG, "caps on a NULL context");
+    for (int on = 1; on >= 0; --on) {
+        CHECK(ar_set_residency_caps(ctx, on) == AR_OK, "set residency caps");
+        int paced = 0, capped = 0;
+        const ar_algo algos[] = {AR_ALGO_RING_FUSED, AR_ALGO_TREE_FUSED,
+                                 AR_ALGO_HALVING_DOUBLING_FUSED, AR_ALGO_DOUBLE_TREE_FUSED};
+        for (int n : {8, 9, 12, 16, 17, 32, 64})
+            for (ar_dtype dt : {AR_INT32, AR_FLOAT32, AR_BFLOAT16})
+                for (ar_op op : {AR_SUM, AR_MAX, AR_AVG})
+                    for (int coll = 0; coll < 2; ++coll)
+                        for (ar_algo algo : algos)
+                            for (size_t mib : {128, 256})
+                                for (long delta : {-17L, 3L, 4096L})
+                                    for (size_t shift : {size_t(0), size_t(4)}) {
+                                        if (dt == AR_INT32 && op == AR_AVG) continue;
+                                        if (algo != AR_ALGO_RING_FUSED && !pow2(n)) continue;
+                                        if ((algo == AR_ALGO_TREE_FUSED ||
+                                             algo == AR_ALGO_DOUBLE_TREE_FUSED) && coll != 0)
+                                            continue;
+                                        const size_t eb = eb_of(dt);
+                                        const size_t count = (size_t)((long)((mib << 20) / eb / n) + delta);
+                                        void* bufs[kMaxN];
+                                        for (int r = 0; r < n; ++r) bufs[r] = rank_addr(r, shift);
+                                        fake_clear_executed();
+                                        const ar_status st = call(ctx, coll, bufs, n, count, dt, op, algo);
+                                        CHECK(st == AR_OK, "capped sweep n=%d dt=%d op=%d coll=%d algo=%d: %d",
+                                              n, (int)dt, (int)op, coll, (int)algo, (int)st);
+                                        for (const FakeLaunch& l : fake_executed()) {
+                                            const unsigned w = fused_waves_per_cu(l.plan);
+                                            paced += fused_variant(l.plan) == CFG_PACED;
+                                            capped += w > 0;
+                                            CHECK(fused_lds_reserve(l.plan) == lds_for_waves(w),
+                                                  "reservation and cap disagree");
+                                        }
                                     }
-                                }
-    CHECK(paced > 100 && capped > paced, "capped shapes barely planned (%d PACED, %d capped)",
-          paced, capped);
+        if (on)
+            CHECK(paced > 100 && capped > paced, "capped shapes barely planned (%d PACED, %d capped)",
+                  paced, capped);
+        else
+            CHECK(paced == 0 && capped == 0, "caps off, yet %d PACED and %d capped plans", paced,
+                  capped);
+    }
+    CHECK(ar_set_residency_caps(ctx, 1) == AR_OK, "caps back on");
 }
 
 void check_residency_caps() {

@@ -183,7 +183,7 @@ hipError_t launch_copy(void*, const void*, size_t, hipStream_t) {
     ++g_count.kernel_launches;
     return hipSuccess;
 }
-hipError_t launch_stream(const void* const*, int, void* const*, int, size_t, hipStream_t) {
+hipError_t launch_stream(const void* const*, int, void* const*, int, size_t, bool, hipStream_t) {
     ++g_count.kernel_launches;
     return hipSuccess;
 }

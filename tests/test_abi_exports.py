@@ -100,6 +100,7 @@ def test_status_strings_and_null_handles():
     assert lib.ar_copy(None, None, None, 16) == 1
     assert lib.ar_set_stream(None, None) == 1
     assert lib.ar_set_graphs(None, 1) == 1
+    assert lib.ar_set_residency_caps(None, 0) == 1
     assert lib.ar_create(None, 0, None) == 1
 
 

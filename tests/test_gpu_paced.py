@@ -124,3 +124,32 @@ def test_threshold_neighbours_agree():
         xs = inputs(dtype, n, count, seed=count)
         want = oracle.ordered_ring_fold(xs, dtype, op)
         assert_bits_equal(run_allreduce(xs, dtype, op, "ring_fused"), want, f"count {count}")
+
+
+def test_caps_off_gives_the_same_bits():
+    """ar_set_residency_caps(0): the same large calls run the uncapped shapes
+    (no LDS reservation) and return the same bits; the calibration stream
+    follows the setting and still writes the XOR of its sources."""
+    n, count = 8, 4 * MIB + 3
+    xs = inputs("float32", n, count, seed=4242)
+    want = oracle.ordered_ring_fold(xs, "float32", "avg")
+    try:
+        ar.set_residency_caps(False)
+        assert_bits_equal(run_allreduce(xs, "float32", "avg", "ring_fused"), want, "caps off")
+        stream_xor_ok()
+    finally:
+        ar.set_residency_caps(True)
+    assert_bits_equal(run_allreduce(xs, "float32", "avg", "ring_fused"), want, "caps on")
+    stream_xor_ok()
+
+
+def stream_xor_ok():
+    # 8 sources just over 128 MiB in all: the paced shape when caps are on
+    srcs = to_gpu(inputs("int32", 8, 4 * MIB + 16, seed=7), "int32")
+    dsts = [torch.empty_like(srcs[0]) for _ in range(2)]
+    ar.stream_(srcs, dsts)
+    torch.cuda.synchronize()
+    x = srcs[0].clone()
+    for t in srcs[1:]:
+        x ^= t
+    assert all(torch.equal(d, x) for d in dsts)
