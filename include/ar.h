@@ -208,8 +208,11 @@ ar_status ar_set_pointer_cache(ar_ctx* ctx, int enable);
  * runs it holds most of each CU's LDS; a caller that overlaps it with kernels
  * needing LDS (GEMMs on another stream) can turn the caps off (enable == 0):
  * the same calls then run the uncapped shapes and reserve no LDS.  Results
- * are bitwise the same either way.  ar_stream follows the setting.  Errors:
- * ctx == NULL -> AR_ERR_INVALID_ARG. */
+ * are bitwise the same either way.  ar_stream follows the setting.  The
+ * reservations are sized for the 160 KiB of LDS per compute unit of gfx950;
+ * on a device that reports another size the caps start off.  Errors: ctx ==
+ * NULL -> AR_ERR_INVALID_ARG; enable != 0 on such a device ->
+ * AR_ERR_UNSUPPORTED (the caps stay off). */
 ar_status ar_set_residency_caps(ar_ctx* ctx, int enable);
 
 /* AllReduce in place: every bufs[r][0:count) ends with the reduction of all

@@ -54,8 +54,10 @@ struct ar_ctx {
     bool ptr_cache = false;
     std::vector<CheckedSet> checked;
     // Residency caps of the fused kernels (ar_set_residency_caps): on unless
-    // the caller turns them off
+    // the caller turns them off or the device's LDS per CU is not the size
+    // they are computed for
     bool caps = true;
+    bool caps_supported = true;
     uint64_t clock = 0;
     // Graph replay of multi-launch collectives (ar_set_graphs): one
     // instantiated graph per (collective, algorithm, shape, pointer set),
@@ -696,6 +698,17 @@ ar_status ar_create(ar_ctx** out, int device, void* stream) {
     c->device = device;
     c->stream = reinterpret_cast<hipStream_t>(stream);
     {
+        // the residency caps size their LDS reservations for kLdsBytesPerCU
+        int lds = 0;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                                  device) != hipSuccess) {
+            (void)hipGetLastError();
+            lds = 0;
+        }
+        c->caps_supported = lds == (int)arlib::kLdsBytesPerCU;
+        c->caps = c->caps_supported;
+    }
+    {
         // ar_check_noalloc's device-resident scratch on this device; a
         // failure here only disables that entry point
         DeviceGuard g(device);
@@ -729,6 +742,10 @@ ar_status ar_set_graphs(ar_ctx* ctx, size_t max_bytes_per_rank) {
 
 ar_status ar_set_residency_caps(ar_ctx* ctx, int enable) {
     if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    if (enable && !ctx->caps_supported)
+        return fail(ctx, AR_ERR_UNSUPPORTED,
+                    "the device's LDS per compute unit is not the %u bytes the caps assume",
+                    arlib::kLdsBytesPerCU);
     ctx->caps = enable != 0;
     return AR_OK;
 }

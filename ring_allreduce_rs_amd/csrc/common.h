@@ -54,9 +54,6 @@ enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_TINY = 2, CFG_PACED = 3 };
 // DEEP is capped above the second.
 constexpr size_t kPacedMinBytes = size_t(128) << 20;
 constexpr size_t kDeepCapMinBytes = size_t(256) << 20;
-// LDS per CU on gfx950: a block that reserves a little over 1/(W+1) of it
-// leaves room for at most W such blocks (one wave each) on the CU.
-constexpr unsigned kLdsBytesPerCU = 160u << 10;
 // Dynamic LDS per one-wave block that lets at most `waves` blocks share a CU:
 // kLdsBytesPerCU / (waves + 1/2), rounded down to 256 bytes (waves fit,
 // waves + 1 do not, with about half a block's share of slack either way).

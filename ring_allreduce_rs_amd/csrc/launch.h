@@ -38,6 +38,12 @@ enum Kind {
 // The tree orders need a power-of-two N.
 enum Order { ORDER_RING = 0, ORDER_PAIR = 1, ORDER_PAIR_BITREV = 2, ORDER_DTREE = 3 };
 
+// LDS per CU on gfx950: a block that reserves a little over 1/(W+1) of it
+// leaves room for at most W such blocks (one wave each) on the CU.  The
+// residency caps rely on it; a context whose device reports another size
+// keeps them off.
+constexpr unsigned kLdsBytesPerCU = 160u << 10;
+
 // Parts the fused kernels split a rank's vector into: N chunks, or the double
 // tree's two halves.
 inline int fused_parts(int order, int nranks) { return order == ORDER_DTREE ? 2 : nranks; }

@@ -606,6 +606,27 @@ void check_capped_launches(ar_ctx* ctx) {
                   capped);
     }
     CHECK(ar_set_residency_caps(ctx, 1) == AR_OK, "caps back on");
+
+    // a device with another LDS size per CU: the caps start off and cannot be
+    // turned on, and the same large call plans no capped launch
+    fake_set_lds_per_cu(64 << 10);
+    ar_ctx* other = nullptr;
+    CHECK(ar_create(&other, 0, nullptr) == AR_OK && other, "create on a 64 KiB-LDS device");
+    if (other) {
+        CHECK(ar_set_residency_caps(other, 1) == AR_ERR_UNSUPPORTED, "caps on a 64 KiB-LDS device");
+        CHECK(ar_set_residency_caps(other, 0) == AR_OK, "caps off on a 64 KiB-LDS device");
+        void* bufs[8];
+        for (int r = 0; r < 8; ++r) bufs[r] = rank_addr(r, 0);
+        fake_clear_executed();
+        CHECK(ar_allreduce(other, bufs, 8, (size_t)64 << 20, AR_FLOAT32, AR_AVG,
+                           AR_ALGO_RING_FUSED) == AR_OK, "large call without caps");
+        for (const FakeLaunch& l : fake_executed())
+            CHECK(fused_variant(l.plan) != CFG_PACED && fused_lds_reserve(l.plan) == 0,
+                  "capped launch on a 64 KiB-LDS device");
+        CHECK(!fake_executed().empty(), "no launch recorded");
+        CHECK(ar_destroy(other) == AR_OK, "destroy");
+    }
+    fake_set_lds_per_cu(160 << 10);
 }
 
 void check_residency_caps() {

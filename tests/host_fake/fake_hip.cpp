@@ -47,6 +47,7 @@ FakeStream g_null_stream;
 std::vector<FakeLaunch> g_executed;
 FakeCounters g_count;
 int g_device = 0;
+int g_lds_per_cu = 160 << 10;   // gfx950
 hipError_t g_last = hipSuccess;
 bool g_coverage_ok = true;
 char g_coverage_msg[512];
@@ -164,6 +165,7 @@ bool fake_coverage_ok(const char** msg) {
     if (msg) *msg = g_coverage_msg;
     return g_coverage_ok;
 }
+void fake_set_lds_per_cu(int bytes) { g_lds_per_cu = bytes; }
 void fake_set_null_stream_capturing(bool on, std::vector<FakeLaunch>* sink) {
     g_null_stream.capturing = on;
     g_null_stream.sink = sink;
@@ -208,6 +210,12 @@ extern "C" {
 
 hipError_t hipGetDeviceCount(int* count) {
     *count = 1;
+    return hipSuccess;
+}
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
+    if (device != 0) return set(hipErrorInvalidDevice);
+    if (attr != hipDeviceAttributeMaxSharedMemoryPerMultiprocessor) return set(hipErrorInvalidValue);
+    *value = g_lds_per_cu;
     return hipSuccess;
 }
 hipError_t hipGetDevice(int* d) {

@@ -33,3 +33,5 @@ FakeCounters& fake_counters();
 bool fake_coverage_ok(const char** msg);
 // Makes the null stream a capturing stream whose launches go to `sink`.
 void fake_set_null_stream_capturing(bool on, std::vector<FakeLaunch>* sink);
+// LDS per compute unit the fake device reports (gfx950: 160 KiB)
+void fake_set_lds_per_cu(int bytes);
