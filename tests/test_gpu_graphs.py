@@ -56,3 +56,43 @@ def test_captured_allreduce_replays_match_oracle(algo, dtype, op):
         want = SIMS[algo](xs, dtype, op).state
         for r in range(n):
             assert_bits_equal(to_np(ts[r]), want[r], f"{algo} replay {rep} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,op,count", [("float32", "avg", (4 << 20) + 3),
+                                            ("bfloat16", "sum", (8 << 20) + 13)])
+def test_captured_capped_allreduce_replays_match_oracle(dtype, op, count):
+    """A call just above 128 MiB runs the residency-capped kernel, whose LDS
+    reservation is part of the recorded launch: every replay matches."""
+    n = 8
+    rng = np.random.Generator(np.random.PCG64(count + 1))
+    inputs = []
+    for rep in range(3):
+        f = [rng.standard_normal(count, dtype=np.float32) for _ in range(n)]
+        inputs.append(f if dtype == "float32" else [
+            torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            for x in f])
+    src = [to_gpu(xs, dtype) for xs in inputs]
+    ts = [torch.empty_like(t) for t in src[0]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for t, s in zip(ts, src[0]):
+            t.copy_(s)
+        ar.allreduce(ts, op=op, algo="ring_fused")      # warm-up on the capture stream
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            ar.allreduce(ts, op=op, algo="ring_fused")
+    torch.cuda.synchronize()
+    for rep, xs in enumerate(inputs):
+        for t, s in zip(ts, src[rep]):                # eager work between replays
+            t.copy_(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = oracle.ordered_ring_fold(xs, dtype, op)
+        for r in (0, n - 1):
+            assert_bits_equal(to_np(ts[r]), want, f"capped replay {rep} rank {r}")
+        assert ar.check(ts)["mismatched"] == 0
+    del src, ts, g
+    torch.cuda.empty_cache()
