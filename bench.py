@@ -56,11 +56,39 @@ KERNEL_SOURCES = [os.path.join(ROOT, "ring_allreduce_rs_amd", "csrc", f)
                             "fused_bf16_lead.hip", "fused_i32_lead.hip", "copy.hip", "dispatch.hip")]
 
 
+def strip_comments(src: str) -> str:
+    """C / C++ source without its comments, whitespace runs collapsed: what
+    the compiler sees, so that editing a comment keeps measurements valid."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the fused kernels' sources (comments excluded): the committed
+    byte counters are reported only while it matches theirs."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -6,12 +6,13 @@ namespace arlib {
 
 int fused_variant(const Plan& p) {
     if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return CFG_WIDE;
-    // Measured on MI355X (fused AllReduce, inputs cold in HBM): WIDE is best
-    // for fp32 / int32 at 8 and 16 ranks (8 x 25 MiB: 74 us vs 83 us DEEP;
-    // 16 x 1 GiB: 6.9 ms vs 7.7 ms); DEEP for 64 ranks (64 x 64 MiB: 1.60 ms
-    // vs 1.88 ms) and for bf16, whose per-hop rounding makes the fold
-    // ALU-heavier and favours the higher occupancy (8 x 2 GiB: 5.97 ms vs
-    // 6.39 ms); small chunks are latency-bound and also favour DEEP.  Beyond
+    // Among the uncapped shapes (measured on MI355X, fused AllReduce, inputs
+    // cold in HBM): WIDE is best for fp32 / int32 at 8 and 16 ranks
+    // (8 x 25 MiB: 74 us vs 83 us DEEP; 16 x 1 GiB: 6.9 ms vs 7.7 ms); DEEP for
+    // 64 ranks (64 x 64 MiB: 1.60 ms vs 1.88 ms) and for bf16, whose per-hop
+    // rounding makes the fold ALU-heavier and favours the higher occupancy
+    // (8 x 2 GiB: 5.97 ms vs 6.39 ms); small chunks are latency-bound and also
+    // favour DEEP.  Large calls then trade WIDE for PACED (below).  Beyond
     // DEEP's 32 ranks of loads per batch, chunks of at most 4 KiB take TINY
     // (every rank's element load in flight at once: 64 x 4 KiB 8.3 -> 5.0 us,
     // 64 x 64 KiB 8.1 -> 5.5 us); at 16 KiB chunks its 4-byte loads lose

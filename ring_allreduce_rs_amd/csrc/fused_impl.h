@@ -306,7 +306,9 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(const Args a) {
 // (p.lead).  On line-aligned layouts both forms are correct; measured on
 // MI355X the LEAD forms ran 0.5-2.8 % faster there on the DEEP and run-time-N
 // WIDE shapes, and 3.7 % slower on the 8-rank WIDE kernel, which therefore
-// keeps the plain indexing when the layout allows it.
+// keeps the plain indexing when the layout allows it.  The 8-rank PACED
+// kernels measured within 0.5 % either way, except ReduceScatter (LEAD 3.7 %
+// slower) and 8 x 200 MiB (LEAD 1.2 % faster): they keep the plain form too.
 inline bool use_lead(const Plan& p) {
     const int cfg = fused_variant(p);
     const bool n8_wide = p.nranks == 8 && (cfg == CFG_WIDE || cfg == CFG_PACED);
