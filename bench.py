@@ -435,15 +435,19 @@ def size_sweep(w):
         count = int(mib * (1 << 20)) // eb
         kb = count * eb
         ws = W.Workload(f"{w.name}@{mib}MiB", n, count, w.dtype, w.dist, w.op)
-        nsets = max(2, -(-4 * INFINITY_CACHE_BYTES // (n * kb)))
+        # at most 32 sets: the binding's pointer-set cache holds 32, and a call
+        # whose set fell out of it re-validates its pointers through the
+        # runtime, which at the small sizes takes longer than the kernel
+        nsets = min(32, max(2, -(-4 * INFINITY_CACHE_BYTES // (n * kb))))
         sets = [W.device_inputs(ws, seed=s) for s in range(nsets)]
         calls = [ar.bind(ts, op=w.op, algo="ring_fused") for ts in sets]
+        streams = [ar.bind_stream(ts, ts) for ts in sets]
         reps = max(20, min(400, int(4e9 // (2 * n * kb))))
         t_f = ev_time(lambda i: calls[i](), nsets, reps)
-        t_s = ev_time(lambda i: ar.stream_(sets[i], sets[i]), nsets, reps)
+        t_s = ev_time(lambda i: streams[i](), nsets, reps)
         flat = [torch.empty(n * kb, dtype=torch.uint8, device="cuda") for _ in range(2 * nsets)]
         t_c = ev_time(lambda i: ar.copy_(flat[2 * i], flat[2 * i + 1]), nsets, reps)
-        del sets, calls, flat
+        del sets, calls, streams, flat
         torch.cuda.empty_cache()
         nbytes = 2 * n * kb
         rows.append((nbytes, t_f, t_s, t_c))

@@ -229,3 +229,19 @@ def bind(tensors, op: str = "sum", algo: str = "ring_fused", kind: str = "allred
         return _Bound(lib.ar_allgather, (ctx.handle, arr, len(ts), count, DTYPES[dt],
                                          ALGOS[algo]), ctx)
     raise ValueError(kind)
+
+
+def bind_stream(srcs, dsts):
+    """Return a zero-argument callable that re-issues the same calibration
+    stream (ar_stream) on the context's current stream (for timing loops)."""
+    bufs = list(srcs) + list(dsts)
+    if not bufs:
+        raise ValueError("bind_stream needs at least one buffer")
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    for t in bufs:
+        if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
+            raise ValueError("bind_stream needs contiguous buffers of one byte size")
+    ctx = context(bufs[0].device.index or 0)
+    sa = (ctypes.c_void_p * max(1, len(srcs)))(*[t.data_ptr() for t in srcs])
+    da = (ctypes.c_void_p * max(1, len(dsts)))(*[t.data_ptr() for t in dsts])
+    return _Bound(lib.ar_stream, (ctx.handle, sa, len(srcs), da, len(dsts), nbytes), ctx)

@@ -177,6 +177,15 @@ def test_calibration_stream_writes_the_xor(nsrc, ndst):
         assert np.array_equal(d.cpu().numpy(), want)
     for s, k in zip(srcs, keep):
         assert torch.equal(s, k)
+    # the pre-bound form (timing loops) issues the same call
+    for d in dsts:
+        d.fill_(-1)
+    call = ar.bind_stream(srcs, dsts)
+    call()
+    call()
+    torch.cuda.synchronize()
+    for d in dsts:
+        assert np.array_equal(d.cpu().numpy(), want)
 
 
 def test_calibration_stream_in_place():
