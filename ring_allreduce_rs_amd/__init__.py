@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import ctypes
 
+from . import _lib
 from ._lib import (  # noqa: F401
     ALGOS, AR_GRAPHS_MAX_BYTES_DEFAULT, AR_MAX_RANKS, DTYPES, EXPORTS, LIB_PATH, OPS, ArError,
     Context, auto_algo, chunk_range, lib, predict_us,
@@ -25,8 +26,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
     "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "dtree_step", "copy_", "stream_",
-    "check", "chunk_range", "bind",
-    "context", "LIB_PATH", "predict_us", "auto_algo", "set_graphs",
+    "check", "chunk_range", "bind", "bind_stream",
+    "context", "LIB_PATH", "predict_us", "auto_algo", "set_graphs", "set_residency_caps",
 ]
 
 _ctx: dict = {}
@@ -200,12 +201,14 @@ def stream_(srcs, dsts):
 
 
 class _Bound:
-    """A pre-marshalled call: the pointer array and enums are built once."""
+    """A pre-marshalled call: the pointer array and enums are converted to
+    ctypes objects once and passed to the entry point as they are."""
 
-    def __init__(self, fn, args, ctx):
+    def __init__(self, fn, args, ctx, *keep):
         self._fn = fn
         self._args = args
         self._ctx = ctx
+        self._keep = keep   # the pointer arrays the arguments point into
 
     def __call__(self):
         st = self._fn(*self._args)
@@ -219,15 +222,16 @@ def bind(tensors, op: str = "sum", algo: str = "ring_fused", kind: str = "allred
     ts, dt, count, dev = _check(tensors)
     ctx = context(dev)
     arr = (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    c_int, h = ctypes.c_int, ctypes.c_void_p(ctx.handle.value)
+    head = (h, arr, c_int(len(ts)), ctypes.c_size_t(count), c_int(DTYPES[dt]))
     if kind == "allreduce":
-        return _Bound(lib.ar_allreduce, (ctx.handle, arr, len(ts), count, DTYPES[dt], OPS[op],
-                                         ALGOS[algo]), ctx)
+        return _Bound(_lib.raw_fn("ar_allreduce"), head + (c_int(OPS[op]), c_int(ALGOS[algo])),
+                      ctx, arr)
     if kind == "reduce_scatter":
-        return _Bound(lib.ar_reduce_scatter, (ctx.handle, arr, len(ts), count, DTYPES[dt],
-                                              OPS[op], ALGOS[algo]), ctx)
+        return _Bound(_lib.raw_fn("ar_reduce_scatter"),
+                      head + (c_int(OPS[op]), c_int(ALGOS[algo])), ctx, arr)
     if kind == "allgather":
-        return _Bound(lib.ar_allgather, (ctx.handle, arr, len(ts), count, DTYPES[dt],
-                                         ALGOS[algo]), ctx)
+        return _Bound(_lib.raw_fn("ar_allgather"), head + (c_int(ALGOS[algo]),), ctx, arr)
     raise ValueError(kind)
 
 
@@ -244,4 +248,7 @@ def bind_stream(srcs, dsts):
     ctx = context(bufs[0].device.index or 0)
     sa = (ctypes.c_void_p * max(1, len(srcs)))(*[t.data_ptr() for t in srcs])
     da = (ctypes.c_void_p * max(1, len(dsts)))(*[t.data_ptr() for t in dsts])
-    return _Bound(lib.ar_stream, (ctx.handle, sa, len(srcs), da, len(dsts), nbytes), ctx)
+    c_int = ctypes.c_int
+    return _Bound(_lib.raw_fn("ar_stream"),
+                  (ctypes.c_void_p(ctx.handle.value), sa, c_int(len(srcs)), da, c_int(len(dsts)),
+                   ctypes.c_size_t(nbytes)), ctx, sa, da)

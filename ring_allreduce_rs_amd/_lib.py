@@ -99,6 +99,17 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
+# The same library's entry points without argtypes, for pre-bound calls whose
+# arguments are converted to ctypes objects once: a call then skips the
+# per-argument conversion checks (about half of a binding call's host time).
+_raw = ctypes.CDLL(LIB_PATH)
+
+
+def raw_fn(name: str):
+    fn = getattr(_raw, name)
+    fn.restype = ctypes.c_int
+    return fn
+
 
 def _status_name(s: int) -> str:
     return lib.ar_status_string(s).decode()
