@@ -41,6 +41,9 @@
  *    reports an allocation's extent; a sub-allocation of a caching allocator
  *    is checked against the whole segment).  ar_set_pointer_cache can trade
  *    that per-call check for a cache of recently checked pointer sets.
+ *  - Large one-pass AllReduce / ReduceScatter calls launch with dynamic LDS
+ *    that no kernel uses for data: it caps the waves resident per compute
+ *    unit (ar_set_residency_caps turns this off).
  */
 #ifndef RING_ALLREDUCE_AR_H
 #define RING_ALLREDUCE_AR_H
