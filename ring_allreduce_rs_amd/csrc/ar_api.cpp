@@ -152,13 +152,16 @@ struct DeviceGuard {
 //   BW       bytes-moved rate of each kernel family; the per-step kernels
 //            re-read what the previous step wrote, partly from the Infinity
 //            Cache, so their rate can exceed a cold stream's; the fused pass
-//            slows as the number of concurrently written rank buffers grows.
+//            slows as the number of concurrently written rank buffers grows
+//            (its rates are those of the residency-capped kernels: 8 ranks
+//            6.25 TB/s over 50 MB - 6.7 GB, 16 ranks 6.0-6.3, 32-64 ranks
+//            5.6-6.1).
 constexpr double kCallUs = 8.0;
 constexpr double kLaunchUs = 3.4;
 constexpr double kStepGBps = 6000.0;
 constexpr double kTreeGBps = 5400.0;
 
-double fused_gbps(int n) { return n <= 8 ? 5500.0 : n <= 16 ? 4950.0 : 4650.0; }
+double fused_gbps(int n) { return n <= 8 ? 6250.0 : n <= 16 ? 6000.0 : 5700.0; }
 
 int log2_ceil(int n) {
     int l = 0;
