@@ -218,6 +218,19 @@ ar_status ar_set_pointer_cache(ar_ctx* ctx, int enable);
  * AR_ERR_UNSUPPORTED (the caps stay off). */
 ar_status ar_set_residency_caps(ar_ctx* ctx, int enable);
 
+/* Residency probe, a diagnostic of the mechanism behind the caps: launches
+ * `blocks` one-wave blocks, each reserving `lds_bytes` of dynamic LDS and
+ * staying resident for a bounded time (about 0.7 ms), and reports the most
+ * blocks found resident at once on a compute unit -- the largest (*max_per_cu)
+ * and the smallest (*min_per_cu) of those per-CU maxima -- and how many
+ * compute units ran a block (*cus).  With lds_bytes the reservation of a cap
+ * W, every CU should hold exactly W.  Synchronous on the context's stream;
+ * allocates and frees 32 KiB of device memory.  Errors: NULL ctx or output,
+ * blocks == 0 or above 1 << 20, lds_bytes above 64 KiB ->
+ * AR_ERR_INVALID_ARG; AR_ERR_NO_MEMORY / AR_ERR_RUNTIME from the runtime. */
+ar_status ar_residency_probe(ar_ctx* ctx, unsigned lds_bytes, unsigned blocks,
+                             unsigned* max_per_cu, unsigned* min_per_cu, unsigned* cus);
+
 /* AllReduce in place: every bufs[r][0:count) ends with the reduction of all
  * ranks' inputs.  RING_STEP and RING_FUSED give identical bits; TREE and
  * HALVING_DOUBLING give their tree-order results. */

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libar.so")
 # compilations run side by side
 SOURCES = ["fused_f32.hip", "fused_f32_lead.hip", "fused_bf16.hip", "fused_bf16_lead.hip",
            "fused_i32.hip", "fused_i32_lead.hip", "fused.hip", "steps.hip", "copy.hip",
-           "check.hip", "dispatch.hip", "ar_api.cpp"]
+           "check.hip", "probe.hip", "dispatch.hip", "ar_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -31,7 +31,7 @@ ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 # every symbol include/ar.h declares
 EXPORTS = (
     "ar_create", "ar_set_stream", "ar_set_graphs", "ar_set_pointer_cache",
-    "ar_set_residency_caps", "ar_allreduce",
+    "ar_set_residency_caps", "ar_residency_probe", "ar_allreduce",
     "ar_reduce_scatter", "ar_allgather", "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step",
     "ar_hd_rs_step", "ar_hd_ag_step", "ar_dtree_step", "ar_chunk_range", "ar_predict_us",
     "ar_auto_algo", "ar_copy", "ar_stream", "ar_check", "ar_check_noalloc", "ar_status_string",
@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "ar_set_graphs": ([vp, sz], i),
         "ar_set_pointer_cache": ([vp, i], i),
         "ar_set_residency_caps": ([vp, i], i),
+        "ar_residency_probe": ([vp, ctypes.c_uint, ctypes.c_uint, ctypes.POINTER(ctypes.c_uint),
+                                ctypes.POINTER(ctypes.c_uint), ctypes.POINTER(ctypes.c_uint)], i),
         "ar_allreduce": ([vp, pp, i, sz, i, i, i], i),
         "ar_reduce_scatter": ([vp, pp, i, sz, i, i, i], i),
         "ar_allgather": ([vp, pp, i, sz, i, i], i),
@@ -172,6 +174,16 @@ class Context:
         """Replay multi-launch collectives of at most this many bytes per rank
         from recorded HIP graphs; 0 turns replay off (ar_set_graphs)."""
         self._check(lib.ar_set_graphs(self._h, max_bytes_per_rank), "ar_set_graphs")
+
+    def residency_probe(self, lds_bytes: int, blocks: int = 256 * 40) -> dict:
+        """The most one-wave blocks a compute unit held at once under an LDS
+        reservation of lds_bytes (ar_residency_probe): the largest and the
+        smallest per-CU maximum and the number of CUs that ran a block."""
+        hi, lo, n = ctypes.c_uint(), ctypes.c_uint(), ctypes.c_uint()
+        self._check(lib.ar_residency_probe(self._h, lds_bytes, blocks, ctypes.byref(hi),
+                                           ctypes.byref(lo), ctypes.byref(n)),
+                    "ar_residency_probe")
+        return {"max_per_cu": hi.value, "min_per_cu": lo.value, "cus": n.value}
 
     def set_residency_caps(self, enable: bool) -> None:
         """Residency caps of the large one-pass calls on (the default) or off

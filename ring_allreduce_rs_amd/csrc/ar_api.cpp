@@ -22,6 +22,7 @@
 
 #include "ar.h"
 #include "launch.h"
+#include "probe.h"
 
 // A pointer set that passed the device-memory checks, with the byte size it
 // was checked for.
@@ -750,6 +751,50 @@ ar_status ar_set_residency_caps(ar_ctx* ctx, int enable) {
                     "the device's LDS per compute unit is not the %u bytes the caps assume",
                     arlib::kLdsBytesPerCU);
     ctx->caps = enable != 0;
+    return AR_OK;
+}
+
+ar_status ar_residency_probe(ar_ctx* ctx, unsigned lds_bytes, unsigned blocks,
+                             unsigned* max_per_cu, unsigned* min_per_cu, unsigned* cus) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    if (!max_per_cu || !min_per_cu || !cus)
+        return fail(ctx, AR_ERR_INVALID_ARG, "NULL output");
+    if (blocks == 0 || blocks > (1u << 20))
+        return fail(ctx, AR_ERR_INVALID_ARG, "blocks %u outside [1, 2^20]", blocks);
+    if (lds_bytes > (64u << 10))
+        return fail(ctx, AR_ERR_INVALID_ARG, "lds_bytes %u above 64 KiB", lds_bytes);
+    DeviceGuard g(ctx->device);
+    if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
+    const size_t table = (size_t)arlib::kProbeSlots * sizeof(unsigned);
+    unsigned* mem = nullptr;
+    if (hipMalloc(reinterpret_cast<void**>(&mem), 2 * table) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_NO_MEMORY, "cannot allocate the probe's tables");
+    }
+    std::vector<unsigned> mx(arlib::kProbeSlots, 0u);
+    hipError_t e = hipMemsetAsync(mem, 0, 2 * table, ctx->stream);
+    if (e == hipSuccess)
+        e = arlib::launch_residency_probe(mem, mem + arlib::kProbeSlots, lds_bytes, blocks, 100,
+                                          ctx->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(mx.data(), mem + arlib::kProbeSlots, table, hipMemcpyDeviceToHost,
+                           ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    (void)hipFree(mem);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, AR_ERR_RUNTIME, "residency probe: %s", hipGetErrorString(e));
+    }
+    unsigned hi = 0, lo = ~0u, n = 0;
+    for (unsigned v : mx) {
+        if (!v) continue;
+        ++n;
+        hi = v > hi ? v : hi;
+        lo = v < lo ? v : lo;
+    }
+    *max_per_cu = hi;
+    *min_per_cu = n ? lo : 0u;
+    *cus = n;
     return AR_OK;
 }
 

@@ -714,6 +714,19 @@ int main() {
         check_graphs(ctx);
         check_checker(ctx);
         check_pointer_cache();
+        // the residency probe: argument checks, and its tables freed again
+        // (no kernel runs here, so no CU reports)
+        unsigned hi = 9, lo = 9, ncu = 9;
+        CHECK(ar_residency_probe(nullptr, 0, 1, &hi, &lo, &ncu) == AR_ERR_INVALID_ARG, "probe NULL ctx");
+        CHECK(ar_residency_probe(ctx, 0, 1, nullptr, &lo, &ncu) == AR_ERR_INVALID_ARG, "probe NULL out");
+        CHECK(ar_residency_probe(ctx, 0, 0, &hi, &lo, &ncu) == AR_ERR_INVALID_ARG, "probe 0 blocks");
+        CHECK(ar_residency_probe(ctx, (64u << 10) + 1, 1, &hi, &lo, &ncu) == AR_ERR_INVALID_ARG,
+              "probe LDS above 64 KiB");
+        const long allocs = fake_counters().device_allocs, frees = fake_counters().device_frees;
+        CHECK(ar_residency_probe(ctx, 29696, 1024, &hi, &lo, &ncu) == AR_OK && hi == 0 && lo == 0 &&
+                  ncu == 0, "probe on the fake device");
+        CHECK(fake_counters().device_allocs - allocs == 1 && fake_counters().device_frees - frees == 1,
+              "probe tables not freed");
         // leave a few graphs recorded: ar_destroy must release them
         CHECK(ar_set_graphs(ctx, SIZE_MAX) == AR_OK, "graphs on");
         void* bufs[kMaxN];
@@ -726,7 +739,8 @@ int main() {
     CHECK(fc.execs_created == fc.execs_destroyed && fc.events_created == fc.events_destroyed &&
               fc.streams_created == fc.streams_destroyed && fc.device_allocs == fc.device_frees,
           "ar_destroy left graphs, events, streams or scratch behind");
-    CHECK(fc.device_allocs == 1 && fc.stream_syncs >= 1, "checker scratch: %ld allocs, %ld syncs",
+    // one allocation for the checker's scratch, one for the residency probe's tables
+    CHECK(fc.device_allocs == 2 && fc.stream_syncs >= 1, "checker scratch: %ld allocs, %ld syncs",
           fc.device_allocs, fc.stream_syncs);
     const char* msg = nullptr;
     CHECK(fake_coverage_ok(&msg), "launch coverage: %s", msg);

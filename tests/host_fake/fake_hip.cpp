@@ -17,6 +17,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <map>
 #include <vector>
 
@@ -185,6 +186,10 @@ hipError_t launch_copy(void*, const void*, size_t, hipStream_t) {
     ++g_count.kernel_launches;
     return hipSuccess;
 }
+hipError_t launch_residency_probe(unsigned*, unsigned*, unsigned, unsigned, int, hipStream_t) {
+    ++g_count.kernel_launches;
+    return hipSuccess;
+}
 hipError_t launch_stream(const void* const*, int, void* const*, int, size_t, bool, hipStream_t) {
     ++g_count.kernel_launches;
     return hipSuccess;
@@ -334,6 +339,15 @@ hipError_t hipFree(void* p) {
         delete[] static_cast<char*>(p);
         ++g_count.device_frees;
     }
+    return hipSuccess;
+}
+hipError_t hipMemsetAsync(void* p, int value, size_t size, hipStream_t) {
+    // fake "device" memory is host memory (hipMalloc above)
+    std::memset(p, value, size);
+    return hipSuccess;
+}
+hipError_t hipMemcpyAsync(void* dst, const void* src, size_t size, hipMemcpyKind, hipStream_t) {
+    std::memcpy(dst, src, size);
     return hipSuccess;
 }
 hipError_t hipStreamSynchronize(hipStream_t) {
