@@ -51,9 +51,11 @@ struct FusedTiny {
 enum { CFG_WIDE = 0, CFG_DEEP = 1, CFG_TINY = 2, CFG_PACED = 3 };
 // Residency caps apply to calls that touch more than these many bytes over
 // all ranks (N x bytes per rank): PACED replaces WIDE above the first, and
-// DEEP is capped above the second.
+// DEEP is capped above the second; the AllGather over more than 8 ranks
+// takes PACED above the third.
 constexpr size_t kPacedMinBytes = size_t(128) << 20;
 constexpr size_t kDeepCapMinBytes = size_t(256) << 20;
+constexpr size_t kAgPacedMinBytes = size_t(512) << 20;
 // Dynamic LDS per one-wave block that lets at most `waves` blocks share a CU:
 // kLdsBytesPerCU / (waves + 1/2), rounded down to 256 bytes (waves fit,
 // waves + 1 do not, with about half a block's share of slack either way).

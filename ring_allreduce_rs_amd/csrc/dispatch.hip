@@ -5,6 +5,19 @@
 namespace arlib {
 
 int fused_variant(const Plan& p) {
+    if (p.kind == KIND_FUSED_AG) {
+        // The AllGather (one read, N - 1 writes per element) takes PACED on
+        // large calls, with the cap below.  Measured on MI355X against WIDE
+        // without a cap: 8 x 25 MiB fp32 37.2 -> 35.6 us, 8 x 200 MiB 305 ->
+        // 269 us, 8 x 2 GiB bf16 3100 -> 2649 us, 16 x 1 GiB int32 3412 ->
+        // 2975 us, 32 x 32 MiB 219 -> 175 us, 64 x 64 MiB 941 -> 719 us.  The
+        // run-time-N form loses on calls of 512 MiB or less (64 x 8 MiB 93.5
+        // -> 97.2 us, 24 x 16 MiB 73.0 -> 75.8, 16 x 9 MiB 26.2 -> 28.7) and
+        // the 8-rank form at 8 x 12.5 MiB (17.9 -> 18.4 us).
+        const size_t total = p.count * (size_t)elem_bytes(p.dtype) * (size_t)p.nranks;
+        const size_t min = p.nranks == kBatch ? kPacedMinBytes : kAgPacedMinBytes;
+        return p.caps && p.vec && p.nranks >= kBatch && total > min ? CFG_PACED : CFG_WIDE;
+    }
     if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return CFG_WIDE;
     // Among the uncapped shapes (measured on MI355X, fused AllReduce, inputs
     // cold in HBM): WIDE is best for fp32 / int32 at 8 and 16 ranks
@@ -60,8 +73,21 @@ int fused_units_per_lane(int cfg) {
 }
 
 unsigned fused_waves_per_cu(const Plan& p) {
-    if (!p.caps || (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS)) return 0;
+    if (!p.caps) return 0;
     const int cfg = fused_variant(p);
+    if (p.kind == KIND_FUSED_AG) {
+        if (cfg != CFG_PACED) return 0;
+        // A wave writes its 1 KiB tile to N - 1 ranks, so the best cap falls
+        // as N grows: about 100-190 KiB of stores in flight per CU.  Sweeps
+        // of 2-28 waves per CU on MI355X: 8 ranks best at 14 (8 x 25 MiB
+        // 35.6 us, 36.4 at 16, 36.7 at 12; 8 x 2 GiB bf16 2649 us, 2743 at
+        // 16, 2694 at 12), 16 at 8 (16 x 1 GiB int32 2975 us, 3008 at 6,
+        // 3037 at 12), 24 at 5 (24 x 32 MiB 138.5 us, 149.5 at 4, 152.1 at
+        // 6), 32 at 4 (32 x 32 MiB 174.8 us, 191.1 at 5, 197.8 at 3), 48 and
+        // 64 at 3 (64 x 64 MiB 719 us, 826 at 2, 754 at 4).
+        return p.nranks <= 8 ? 14 : p.nranks <= 16 ? 8 : p.nranks <= 24 ? 5 : p.nranks <= 32 ? 4 : 3;
+    }
+    if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return 0;
     // How many waves a CU needs depends on the bytes a wave keeps in flight
     // and on the fold's ALU work per byte: the IEEE maximum of fp32 / bf16
     // (NaN handling, bf16 widening) wants more waves than an add or an

@@ -7,13 +7,33 @@ namespace arlib {
 template <int EB>
 static hipError_t launch_fused_ag(const Plan& p, const Args& a, dim3 grid, hipStream_t s) {
     const dim3 block(kFusedThreads);
+    // large calls: one unit per lane under a residency cap (fused_variant,
+    // fused_waves_per_cu), the reservation being dynamic LDS no kernel reads
+    const bool paced = fused_variant(p) == CFG_PACED;
+    const unsigned lds = fused_lds_reserve(p);
     // 8 ranks: the rank loop unrolled, in the line-aligned form whatever the
     // layout (lead 0 when the layout is aligned).  Measured on MI355X against
     // the run-time-N kernel: 8 x 25 MiB fp32 37.2 vs 38.9 us, bf16 -2 %,
     // ragged counts -1.6 %; the plain 8-rank form was slower (40.1 us).
     if (p.vec && p.nranks == 8) {
-        hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 8, FusedWide, ORDER_RING, true>),
-                           grid, block, 0, s, a);
+        if (paced)
+            hipLaunchKernelGGL(
+                (k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 8, FusedPaced, ORDER_RING, true>), grid,
+                block, lds, s, a);
+        else
+            hipLaunchKernelGGL(
+                (k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 8, FusedWide, ORDER_RING, true>), grid,
+                block, 0, s, a);
+        return hipGetLastError();
+    }
+    if (paced) {
+        if (p.lead)
+            hipLaunchKernelGGL(
+                (k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 0, FusedPaced, ORDER_RING, true>), grid,
+                block, lds, s, a);
+        else
+            hipLaunchKernelGGL((k_fused<OpCopy<EB>, KIND_FUSED_AG, true, 0, FusedPaced>), grid,
+                               block, lds, s, a);
         return hipGetLastError();
     }
     if (p.vec && p.lead)

@@ -598,6 +598,32 @@ void check_capped_launches(ar_ctx* ctx) {
                                                   "reservation and cap disagree");
                                         }
                                     }
+        // the AllGather around its two thresholds (8 ranks: 128 MiB over all
+        // ranks; more ranks: 512 MiB), ring and halving-doubling algos
+        int ag_paced = 0;
+        for (int n : {8, 12, 16, 24, 32, 64})
+            for (ar_dtype dt : {AR_INT32, AR_BFLOAT16})
+                for (ar_algo algo : {AR_ALGO_RING_FUSED, AR_ALGO_HALVING_DOUBLING_FUSED})
+                    for (size_t mib : {128, 512})
+                        for (long delta : {-17L, 3L, 4096L})
+                            for (size_t shift : {size_t(0), size_t(4)}) {
+                                if (algo != AR_ALGO_RING_FUSED && !pow2(n)) continue;
+                                const size_t count = (size_t)((long)((mib << 20) / eb_of(dt) / n) + delta);
+                                void* bufs[kMaxN];
+                                for (int r = 0; r < n; ++r) bufs[r] = rank_addr(r, shift);
+                                fake_clear_executed();
+                                CHECK(call(ctx, 2, bufs, n, count, dt, AR_SUM, algo) == AR_OK,
+                                      "AllGather sweep n=%d dt=%d algo=%d", n, (int)dt, (int)algo);
+                                for (const FakeLaunch& l : fake_executed()) {
+                                    const unsigned w = fused_waves_per_cu(l.plan);
+                                    ag_paced += fused_variant(l.plan) == CFG_PACED;
+                                    CHECK(fused_lds_reserve(l.plan) == lds_for_waves(w),
+                                          "AllGather reservation and cap disagree");
+                                    CHECK((w > 0) == (fused_variant(l.plan) == CFG_PACED),
+                                          "AllGather cap without PACED");
+                                }
+                            }
+        CHECK(on ? ag_paced > 20 : ag_paced == 0, "AllGather PACED plans: %d (caps %d)", ag_paced, on);
         if (on)
             CHECK(paced > 100 && capped > paced, "capped shapes barely planned (%d PACED, %d capped)",
                   paced, capped);
@@ -632,12 +658,12 @@ void check_capped_launches(ar_ctx* ctx) {
 void check_residency_caps() {
     using namespace arlib;
     int paced = 0, capped = 0;
-    for (int n : {2, 4, 7, 8, 9, 16, 17, 32, 64})
+    for (int n : {2, 4, 7, 8, 9, 16, 17, 24, 25, 32, 33, 64})
         for (int dt : {AR_INT32, AR_FLOAT32, AR_BFLOAT16})
             for (int op : {AR_SUM, AR_MAX, AR_AVG})
                 for (int kind : {KIND_FUSED_AR, KIND_FUSED_RS, KIND_FUSED_AG})
                     for (int order : {ORDER_RING, ORDER_PAIR, ORDER_PAIR_BITREV, ORDER_DTREE})
-                        for (size_t mib : {1, 16, 64, 127, 129, 300, 4096})
+                        for (size_t mib : {1, 16, 64, 127, 129, 300, 511, 513, 4096})
                             for (bool vec : {false, true}) {
                                 if (order != ORDER_RING && !pow2(n)) continue;
                                 Plan p{};
@@ -658,9 +684,19 @@ void check_residency_caps() {
                                 const bool bf16_ok = dt != AR_BFLOAT16 ||
                                                      (n == kBatch && kind == KIND_FUSED_AR &&
                                                       order == ORDER_RING && op != AR_MAX);
-                                if (cfg == CFG_PACED)
-                                    CHECK(n >= kBatch && vec && bf16_ok && total > kPacedMinBytes &&
-                                              kind != KIND_FUSED_AG,
+                                // the AllGather (a copy: any dtype, and the order
+                                // plays no part), a higher threshold beyond 8 ranks
+                                const size_t ag_min = n == kBatch ? kPacedMinBytes : kAgPacedMinBytes;
+                                const bool ag_paced = kind == KIND_FUSED_AG && n >= kBatch && vec &&
+                                                      total > ag_min;
+                                if (kind == KIND_FUSED_AG)
+                                    CHECK((cfg == CFG_PACED) == ag_paced && (cfg == CFG_PACED || cfg == CFG_WIDE),
+                                          "AllGather shape n=%d total=%zu cfg=%d", n, total, cfg);
+                                if (cfg == CFG_PACED && kind == KIND_FUSED_AG)
+                                    CHECK(w == (n <= 8 ? 14u : n <= 16 ? 8u : n <= 24 ? 5u : n <= 32 ? 4u : 3u),
+                                          "AllGather cap %u at n=%d", w, n);
+                                if (cfg == CFG_PACED && kind != KIND_FUSED_AG)
+                                    CHECK(n >= kBatch && vec && bf16_ok && total > kPacedMinBytes,
                                           "PACED n=%d dt=%d kind=%d total=%zu", n, dt, kind, total);
                                 if (cfg != CFG_PACED && dt == AR_BFLOAT16 && n == kBatch && vec &&
                                     kind == KIND_FUSED_AR && order == ORDER_RING && op != AR_MAX &&
@@ -669,7 +705,7 @@ void check_residency_caps() {
                                 if (kind == KIND_FUSED_AR && n >= kBatch && vec && dt != AR_BFLOAT16 &&
                                     total > kPacedMinBytes && (cfg == CFG_WIDE))
                                     CHECK(false, "WIDE kept above the threshold n=%d", n);
-                                if (kind == KIND_FUSED_AG || cfg == CFG_WIDE || cfg == CFG_TINY)
+                                if (cfg == CFG_WIDE || cfg == CFG_TINY)
                                     CHECK(w == 0 && lds == 0, "uncapped shape reserves LDS");
                                 if (cfg == CFG_PACED) {
                                     CHECK(w >= 3, "PACED without a cap");
@@ -684,8 +720,8 @@ void check_residency_caps() {
                                 CHECK(kLdsBytesPerCU / lds == w, "cap %u but %u blocks fit (lds %u)",
                                       w, kLdsBytesPerCU / lds, lds);
                                 // slack for a coarser allocation granule: rounding
-                                // the reservation up by 1 KiB still fits w blocks
-                                CHECK(kLdsBytesPerCU / (lds + 1024) == w, "cap %u too tight", w);
+                                // the reservation up by 256 bytes still fits w blocks
+                                CHECK(kLdsBytesPerCU / (lds + 256) == w, "cap %u too tight", w);
                                 ++capped;
                             }
     CHECK(paced > 50 && capped > paced, "caps barely exercised (%d PACED, %d capped)", paced, capped);

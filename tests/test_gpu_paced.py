@@ -3,13 +3,15 @@
 The PACED shape (one 16-byte unit per lane, an LDS reservation capping the
 waves per compute unit) and the capped DEEP shape only run on calls above a
 size threshold: more than 128 MiB over all ranks for PACED, 256 MiB for the
-DEEP cap.  Each case here sits just above its threshold and picks one kernel
-form: the compiled 8-rank loop or the run-time rank count, plain or
-line-aligned indexing (ragged counts put chunk starts off 16-byte units and
-off 128-byte lines), every fold order, ReduceScatter, every dtype and op, and
-AVG with a rank count that is not a power of two.  Every position of rank 0
-is compared bit for bit with the oracle's fold; the on-device checker
-confirms that every rank holds the same bits.
+DEEP cap, 512 MiB for the AllGather's PACED shape beyond 8 ranks.  Each case
+here sits just above its threshold and picks one kernel form: the compiled
+8-rank loop or the run-time rank count, plain or line-aligned indexing (ragged
+counts put chunk starts off 16-byte units and off 128-byte lines), every fold
+order, ReduceScatter, AllGather under each of its caps, every dtype and op,
+and AVG with a rank count that is not a power of two.  For the AllReduce every
+position of rank 0 is compared bit for bit with the oracle's fold and the
+on-device checker confirms that every rank holds the same bits; the
+AllGather compares every rank with the oracle's ring AllGather.
 """
 
 import numpy as np
@@ -116,6 +118,37 @@ def test_capped_reduce_scatter_matches_oracle(n, dtype, op, count):
     torch.cuda.empty_cache()
 
 
+# AllGather over PACED: (ranks, dtype, count), each just above its threshold
+# (8 ranks: 128 MiB over all ranks; more ranks: 512 MiB): the 8-rank loop, the
+# run-time rank count with plain and line-aligned indexing, every cap
+AG_CASES = [
+    (8, "float32", 4 * MIB + 3),            # 8-rank loop, ragged chunks
+    (8, "bfloat16", 8 * MIB + 1024),        # 8-rank loop, aligned chunks
+    (16, "int32", 8 * MIB + 512),           # run-time N, plain indexing (cap 8)
+    (16, "float32", 8 * MIB + 5),           # run-time N, line-aligned (cap 8)
+    (24, "int32", 5592406),                 # cap 5
+    (32, "bfloat16", 8 * MIB + 77),         # cap 4
+    (64, "float32", 2 * MIB + 7),           # cap 3
+]
+
+
+@pytest.mark.parametrize("n,dtype,count", AG_CASES,
+                         ids=[f"n{c[0]}-{c[1]}-{c[2]}" for c in AG_CASES])
+def test_capped_allgather_matches_oracle(n, dtype, count):
+    threshold = 128 * MIB if n == 8 else 512 * MIB
+    assert total_bytes(dtype, n, count) > threshold
+    xs = inputs(dtype, n, count, seed=n * 7 + count)
+    want = oracle.simulate_ring_allgather(xs, dtype).state
+    ts = to_gpu(xs, dtype)
+    del xs
+    ar.allgather(ts, algo="ring_fused")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bits_equal(to_np(ts[r]), want[r], f"AllGather rank {r}")
+    del ts
+    torch.cuda.empty_cache()
+
+
 def test_threshold_neighbours_agree():
     """The same AllReduce just below (uncapped WIDE) and just above (PACED)
     the threshold: both equal the oracle, so the shape switch is invisible."""
@@ -137,10 +170,21 @@ def test_caps_off_gives_the_same_bits():
         ar.set_residency_caps(False)
         assert_bits_equal(run_allreduce(xs, "float32", "avg", "ring_fused"), want, "caps off")
         stream_xor_ok()
+        allgather_ok(xs)
     finally:
         ar.set_residency_caps(True)
     assert_bits_equal(run_allreduce(xs, "float32", "avg", "ring_fused"), want, "caps on")
     stream_xor_ok()
+    allgather_ok(xs)
+
+
+def allgather_ok(xs):
+    want = oracle.simulate_ring_allgather(xs, "float32").state
+    ts = to_gpu(xs, "float32")
+    ar.allgather(ts, algo="ring_fused")
+    torch.cuda.synchronize()
+    for r in range(len(xs)):
+        assert_bits_equal(to_np(ts[r]), want[r], f"AllGather rank {r}")
 
 
 def stream_xor_ok():

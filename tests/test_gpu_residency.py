@@ -12,7 +12,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 LDS_PER_CU = 160 << 10
-CAPS = [3, 4, 5, 6, 7, 10]     # every cap the library chooses
+CAPS = [3, 4, 5, 6, 7, 8, 10, 14]     # every cap the library chooses
 
 
 def reservation(w):
