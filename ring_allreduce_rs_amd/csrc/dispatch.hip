@@ -138,6 +138,26 @@ unsigned fused_waves_per_cu(const Plan& p) {
         // int32 MAX 464 -> 383 us (all at 3)
         return 3;
     }
+    if (cfg == CFG_DEEP && p.kind == KIND_FUSED_RS) {
+        // The ReduceScatter issues the AllReduce's loads but stores once per
+        // element, so its caps sit higher.  Beyond 16 ranks, measured
+        // uncapped -> capped (calls of 256 MiB or less lose: 64 x 4 MiB int32
+        // 50.3 -> 52.6 us at 5):
+        const size_t total = p.count * (size_t)elem_bytes(p.dtype) * (size_t)p.nranks;
+        if (total <= kDeepCapMinBytes || p.nranks <= 16) return 0;
+        if (p.dtype == AR_BFLOAT16) {
+            // bf16 MAX: 64 x 16 MiB 220.8 us uncapped, 242.1 at 10; SUM /
+            // AVG: 64 x 16 MiB 193.8 -> 185.7 us, 32 x 32 MiB 181.8 -> 175.4
+            // (8; 198 at 6, 179 at 10)
+            return p.op == AR_MAX ? 0 : 8;
+        }
+        // fp32 MAX: 64 x 16 MiB 194.6 -> 188.5 us (8; 187.0 at 10, 217.8 at
+        // 6); fp32 SUM / AVG, int32 SUM / MAX at 5: 64 x 16 MiB 191.7 ->
+        // 172.3 us, 64 x 8 MiB 98.2 -> 91.5, 32 x 32 MiB 179.5 -> 167.9,
+        // 32 x 32 MiB int32 MAX 181.5 -> 168.9, 64 x 64 MiB 684.5 -> 656.4
+        // (4 and 6 within 1-3 % of 5, 3 and 10 worse)
+        return fmax ? 8 : 5;
+    }
     return 0;
 }
 

@@ -96,10 +96,15 @@ def test_capped_tree_orders_match_oracle(dtype, op):
         assert_bits_equal(run_allreduce(xs, dtype, op, algo), want, f"{algo} {dtype} {op}")
 
 
-# ReduceScatter over PACED (its own cap): each owner's chunk
+# ReduceScatter over PACED and over capped DEEP (beyond 16 ranks and 256 MiB):
+# each owner's chunk
 @pytest.mark.parametrize("n,dtype,op,count", [(8, "float32", "sum", 4 * MIB + 3),
                                               (16, "int32", "max", 2 * MIB + 9),
-                                              (8, "int32", "sum", 4 * MIB + 4096)])
+                                              (8, "int32", "sum", 4 * MIB + 4096),
+                                              (32, "float32", "avg", 2 * MIB + 3),
+                                              (64, "float32", "max", MIB + 5),
+                                              (32, "bfloat16", "sum", 4 * MIB + 7),
+                                              (24, "int32", "max", 2796203)])
 def test_capped_reduce_scatter_matches_oracle(n, dtype, op, count):
     assert total_bytes(dtype, n, count) > 128 * MIB
     xs = inputs(dtype, n, count, seed=n + count)
