@@ -41,9 +41,9 @@
  *    reports an allocation's extent; a sub-allocation of a caching allocator
  *    is checked against the whole segment).  ar_set_pointer_cache can trade
  *    that per-call check for a cache of recently checked pointer sets.
- *  - Large one-pass AllReduce / ReduceScatter calls launch with dynamic LDS
- *    that no kernel uses for data: it caps the waves resident per compute
- *    unit (ar_set_residency_caps turns this off).
+ *  - Large one-pass AllReduce / ReduceScatter / AllGather calls launch with
+ *    dynamic LDS that no kernel uses for data: it caps the waves resident
+ *    per compute unit (ar_set_residency_caps turns this off).
  */
 #ifndef RING_ALLREDUCE_AR_H
 #define RING_ALLREDUCE_AR_H
@@ -204,10 +204,12 @@ ar_status ar_set_pointer_cache(ar_ctx* ctx, int enable);
 
 /* Residency caps of the one-pass kernels (on by default).  Large one-pass
  * AllReduce / ReduceScatter calls (more than 128 MiB over all ranks, from 8
- * ranks up; DEEP shapes above 256 MiB) launch with dynamic LDS that no kernel
- * touches, so that only 3-10 of their one-wave blocks fit on a compute unit
- * at once: fewer, smaller memory requests per CU stream HBM faster (on
- * MI355X, 8 x 25 MiB fp32: 70 us capped, 75 us uncapped).  While such a call
+ * ranks up; DEEP shapes above 256 MiB) and AllGather calls (from 8 ranks up,
+ * more than 128 MiB at 8 ranks and 512 MiB beyond) launch with dynamic LDS
+ * that no kernel touches, so that only 3-14 of their one-wave blocks fit on
+ * a compute unit at once: fewer, smaller memory requests per CU stream HBM
+ * faster (on MI355X, 8 x 25 MiB fp32 AllReduce: 70 us capped, 75 us
+ * uncapped).  While such a call
  * runs it holds most of each CU's LDS; a caller that overlaps it with kernels
  * needing LDS (GEMMs on another stream) can turn the caps off (enable == 0):
  * the same calls then run the uncapped shapes and reserve no LDS.  Results
