@@ -137,6 +137,11 @@ def parse():
                          "stream and the plain copy over the same bytes, for the workload's rank "
                          "count and dtype at sizes per rank from 0.78 to 400 MiB, and fit "
                          "T = a + bytes / BW to each (one JSON line per size, then one fit line)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-block timeline of the in-place N-read / N-write calibration stream "
+                         "at the workload's size (ar_stream_timeline), under the one-pass ring's "
+                         "residency cap and without: steady streaming rate, ramp and drain (one "
+                         "JSON line per launch)")
     a = ap.parse_args()
     return a, names[a.workload]
 
@@ -474,6 +479,61 @@ def size_sweep(w):
           flush=True)
 
 
+def lds_for_waves(waves):
+    """The LDS reservation that holds a compute unit at `waves` one-wave blocks:
+    160 KiB / (waves + 1/2), rounded down to 256 bytes (0: no reservation)."""
+    return 0 if waves == 0 else (2 * (160 << 10) // (2 * waves + 1)) & ~255
+
+
+def timeline(w, caps=(5, 0), launches=24, keep=4):
+    """Where a one-pass launch spends its time: the in-place calibration stream
+    over the workload's buffers (the fused AllReduce's access pattern without
+    the reduction) with a per-block start / end on the device's wall clock."""
+    import numpy as np
+    import torch
+
+    import ring_allreduce_rs_amd as ar
+
+    n = w.nranks
+    nbytes = w.count * w.itemsize // 16 * 16
+    nsets = max(2, -(-4 * INFINITY_CACHE_BYTES // (n * nbytes)))
+    sets = [[torch.full((nbytes // 4,), s * n + r, dtype=torch.int32, device="cuda")
+             for r in range(n)] for s in range(nsets)]
+    blocks = -(-nbytes // 1024)
+    ts = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    per_block = 2 * n * 1024          # bytes one block reads and writes
+    for waves in caps:
+        lds = lds_for_waves(waves)
+        for it in range(launches):
+            nblk, khz = ar.stream_timeline(sets[it % nsets], lds, ts)
+            if it < launches - keep:
+                continue
+            torch.cuda.synchronize()
+            t = ts.view(-1, 2).cpu().numpy().astype(np.float64) / (khz / 1e3)   # us
+            t -= t[:, 0].min()
+            start, end = t[:, 0], t[:, 1]
+            span = float(end.max())
+            lo, hi = 0.25 * span, 0.75 * span
+            rate = float(((end >= lo) & (end < hi)).sum()) / (hi - lo)          # blocks per us
+            resident = float((np.clip(end, lo, hi) - np.clip(start, lo, hi)).sum()) / (hi - lo)
+            edges = np.linspace(0.0, span, 21)
+            active = [int(((start <= x) & (end > x)).sum()) for x in edges[:-1]]
+            steady = rate * per_block / 1e3                                    # GB/s
+            print(json.dumps({
+                "timeline": w.name, "waves_per_cu_cap": waves or None, "lds_bytes": lds,
+                "blocks": nblk, "bytes_moved": 2 * n * nbytes, "span_us": round(span, 2),
+                "span_frac_hbm_peak": round(2 * n * nbytes / span / 1e3 / HBM_PEAK_GBPS, 4),
+                "steady_blocks_per_us": round(rate, 1), "steady_GBps": round(steady, 1),
+                "steady_frac_hbm_peak": round(steady / HBM_PEAK_GBPS, 4),
+                "us_over_steady": round(span - nblk / rate, 2),
+                "first_block_done_us": round(float(end.min()), 2),
+                "last_block_start_us": round(float(start.max()), 2),
+                "block_us_p10_p50_p90": [round(float(np.percentile(end - start, q)), 2)
+                                         for q in (10, 50, 90)],
+                "resident_blocks_mid": round(resident, 1),
+                "active_blocks_per_5pct_of_span": active}), flush=True)
+
+
 def main():
     args, w = parse()
     if args.gpus != 1:
@@ -485,6 +545,8 @@ def main():
         return sweep(args)
     if args.size_sweep:
         return size_sweep(w)
+    if args.timeline:
+        return timeline(w)
     import numpy as np
     import torch
 

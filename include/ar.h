@@ -345,6 +345,27 @@ ar_status ar_copy(ar_ctx* ctx, void* dst, const void* src, size_t bytes);
 ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* dst, int ndst,
                     size_t bytes);
 
+/* Timeline of the calibration stream, a diagnostic of where a one-pass
+ * kernel's time goes: the in-place N-read / N-write XOR stream of ar_stream
+ * over bufs[0..nbufs) (each buffer read, then overwritten with the XOR of all
+ * of them) in the paced shape: one 64-lane block per 1 KiB tile of every
+ * buffer, one 16-byte unit per lane, launched with lds_bytes of dynamic LDS
+ * per block (0: none) to cap the blocks resident per compute unit.  Block b
+ * writes the device's constant-rate wall clock at its start to ts[2b] and,
+ * once all of its loads and stores have completed, to ts[2b + 1]; from them a
+ * caller reads the ramp, the steady rate and the drain of the launch.
+ * bufs is a HOST array of DEVICE pointers, 16-byte aligned, device memory of
+ * the context's device, not overlapping; bytes > 0, a multiple of 16; ts is
+ * DEVICE memory of that device, 8-byte aligned, holding ts_len >= 2 *
+ * ceil(bytes / 1024) entries, overlapping no buffer.  *blocks (if not NULL)
+ * receives ceil(bytes / 1024), *clock_khz (if not NULL) the clock's rate in
+ * kHz.  Enqueued on the context's stream.  Errors: AR_ERR_INVALID_ARG for any
+ * of the above or lds_bytes above 64 KiB; AR_ERR_RUNTIME if the launch
+ * fails. */
+ar_status ar_stream_timeline(ar_ctx* ctx, void* const* bufs, int nbufs, size_t bytes,
+                             unsigned lds_bytes, unsigned long long* ts, size_t ts_len,
+                             size_t* blocks, unsigned* clock_khz);
+
 /* On-device check of an AllReduce result, a test utility: the whole array is
  * checked where it lies, without copying it to the host.  An AllReduce leaves
  * every participant with the same data ("AllReduce", compassingai.com,

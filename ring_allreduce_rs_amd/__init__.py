@@ -26,7 +26,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "ArError", "Context", "allreduce", "reduce_scatter", "allgather", "ring_rs_step",
     "ring_ag_step", "tree_step", "hd_rs_step", "hd_ag_step", "dtree_step", "copy_", "stream_",
-    "check", "chunk_range", "bind", "bind_stream",
+    "check", "chunk_range", "bind", "bind_stream", "stream_timeline",
     "context", "LIB_PATH", "predict_us", "auto_algo", "set_graphs", "set_residency_caps",
 ]
 
@@ -233,6 +233,24 @@ def bind(tensors, op: str = "sum", algo: str = "ring_fused", kind: str = "allred
     if kind == "allgather":
         return _Bound(_lib.raw_fn("ar_allgather"), head + (c_int(ALGOS[algo]),), ctx, arr)
     raise ValueError(kind)
+
+
+def stream_timeline(bufs, lds_bytes, ts):
+    """Timeline of the in-place calibration stream over `bufs` (ar_stream_timeline):
+    each buffer is overwritten with the XOR of all of them, block b writes its
+    start and end on the device's wall clock to ts[2b], ts[2b + 1] (ts: an int64
+    tensor on the same device).  Returns (blocks, clock rate in kHz)."""
+    bufs = list(bufs)
+    if not bufs:
+        raise ValueError("stream_timeline needs at least one buffer")
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    for t in bufs:
+        if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
+            raise ValueError("stream_timeline needs contiguous buffers of one byte size")
+    if not ts.is_contiguous() or ts.element_size() != 8:
+        raise ValueError("ts must be a contiguous 8-byte tensor")
+    return context(bufs[0].device.index or 0).stream_timeline_ptrs(
+        [t.data_ptr() for t in bufs], nbytes, lds_bytes, ts.data_ptr(), ts.numel())
 
 
 def bind_stream(srcs, dsts):

@@ -34,7 +34,8 @@ EXPORTS = (
     "ar_set_residency_caps", "ar_residency_probe", "ar_allreduce",
     "ar_reduce_scatter", "ar_allgather", "ar_ring_rs_step", "ar_ring_ag_step", "ar_tree_step",
     "ar_hd_rs_step", "ar_hd_ag_step", "ar_dtree_step", "ar_chunk_range", "ar_predict_us",
-    "ar_auto_algo", "ar_copy", "ar_stream", "ar_check", "ar_check_noalloc", "ar_status_string",
+    "ar_auto_algo", "ar_copy", "ar_stream", "ar_stream_timeline", "ar_check", "ar_check_noalloc",
+    "ar_status_string",
     "ar_last_error", "ar_destroy",
 )
 
@@ -86,6 +87,8 @@ def _load() -> ctypes.CDLL:
         "ar_auto_algo": ([i, sz, i, ctypes.POINTER(i)], i),
         "ar_copy": ([vp, vp, vp, sz], i),
         "ar_stream": ([vp, pp, i, pp, i, sz], i),
+        "ar_stream_timeline": ([vp, pp, i, sz, ctypes.c_uint, vp, sz, ctypes.POINTER(sz),
+                                ctypes.POINTER(ctypes.c_uint)], i),
         "ar_check": ([vp, pp, i, sz, i, vp, vp, vp], i),
         "ar_check_noalloc": ([vp, pp, i, sz, i, vp, vp, vp], i),
         "ar_status_string": ([i], cp),
@@ -259,6 +262,14 @@ class Context:
     def stream_ptrs(self, srcs, dsts, nbytes):
         self._check(lib.ar_stream(self._h, _ptr_array(srcs), len(srcs), _ptr_array(dsts),
                                   len(dsts), nbytes), "ar_stream")
+
+    def stream_timeline_ptrs(self, ptrs, nbytes, lds_bytes, ts_ptr, ts_len):
+        """ar_stream_timeline: returns (blocks, wall-clock kHz)."""
+        blocks, khz = ctypes.c_size_t(), ctypes.c_uint()
+        self._check(lib.ar_stream_timeline(self._h, _ptr_array(ptrs), len(ptrs), nbytes,
+                                           lds_bytes, ts_ptr, ts_len, ctypes.byref(blocks),
+                                           ctypes.byref(khz)), "ar_stream_timeline")
+        return blocks.value, khz.value
 
     def close(self) -> None:
         if self._h:

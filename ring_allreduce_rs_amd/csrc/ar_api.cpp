@@ -949,6 +949,69 @@ ar_status ar_stream(ar_ctx* ctx, const void* const* src, int nsrc, void* const* 
     }
 }
 
+ar_status ar_stream_timeline(ar_ctx* ctx, void* const* bufs, int nbufs, size_t bytes,
+                             unsigned lds_bytes, unsigned long long* ts, size_t ts_len,
+                             size_t* blocks, unsigned* clock_khz) {
+    if (!ctx) return fail(nullptr, AR_ERR_INVALID_ARG, "ctx is NULL");
+    try {
+        if (!bufs || !ts) return fail(ctx, AR_ERR_INVALID_ARG, "NULL bufs or ts");
+        if (nbufs < 1 || nbufs > AR_MAX_RANKS)
+            return fail(ctx, AR_ERR_INVALID_ARG, "nbufs %d outside [1, %d]", nbufs, AR_MAX_RANKS);
+        if (bytes == 0 || bytes % 16)
+            return fail(ctx, AR_ERR_INVALID_ARG, "bytes %zu is 0 or not a multiple of 16", bytes);
+        if (lds_bytes > (64u << 10))
+            return fail(ctx, AR_ERR_INVALID_ARG, "lds_bytes %u above 64 KiB", lds_bytes);
+        if (reinterpret_cast<uintptr_t>(ts) & 7u)
+            return fail(ctx, AR_ERR_INVALID_ARG, "ts is not 8-byte aligned");
+        const size_t nblk = (bytes + 1023) / 1024;   // one 1 KiB tile per buffer per block
+        if (nblk > 0x7fffffffu)
+            return fail(ctx, AR_ERR_INVALID_ARG, "bytes %zu needs more than 2^31 blocks", bytes);
+        if (ts_len < 2 * nblk)
+            return fail(ctx, AR_ERR_INVALID_ARG, "ts_len %zu below 2 x %zu blocks", ts_len, nblk);
+        for (int i = 0; i < nbufs; ++i)
+            if (reinterpret_cast<uintptr_t>(bufs[i]) & 15u)
+                return fail(ctx, AR_ERR_INVALID_ARG, "bufs[%d] is not 16-byte aligned", i);
+        bool vec;
+        unsigned mis;
+        ar_status st = check_buffers(ctx, bufs, nbufs, bytes / 4, AR_INT32, &vec, &mis);
+        if (st != AR_OK) return st;
+        void* tsp = ts;
+        const size_t ts_bytes = 2 * nblk * sizeof(unsigned long long);
+        st = check_buffers(ctx, &tsp, 1, ts_bytes / 4, AR_INT32, &vec, &mis);
+        if (st != AR_OK) return st;
+        const uintptr_t t0 = reinterpret_cast<uintptr_t>(ts);
+        for (int i = 0; i < nbufs; ++i) {
+            const uintptr_t b = reinterpret_cast<uintptr_t>(bufs[i]);
+            if (t0 < b + bytes && b < t0 + ts_bytes)
+                return fail(ctx, AR_ERR_INVALID_ARG, "ts overlaps bufs[%d]", i);
+        }
+        DeviceGuard g(ctx->device);
+        if (!g.ok) return fail(ctx, AR_ERR_RUNTIME, "cannot select device %d", ctx->device);
+        if (clock_khz) {
+            int khz = 0;
+            if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, ctx->device) !=
+                    hipSuccess ||
+                khz <= 0) {
+                (void)hipGetLastError();
+                return fail(ctx, AR_ERR_RUNTIME, "cannot read the wall-clock rate");
+            }
+            *clock_khz = (unsigned)khz;
+        }
+        const hipError_t e =
+            arlib::launch_stream_timeline(bufs, nbufs, bytes, lds_bytes, ts, ctx->stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ctx, AR_ERR_RUNTIME, "timeline launch failed: %s", hipGetErrorString(e));
+        }
+        if (blocks) *blocks = nblk;
+        return AR_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(ctx, AR_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(ctx, AR_ERR_RUNTIME, "unexpected exception");
+    }
+}
+
 namespace {
 
 // ar_check and ar_check_noalloc: the same validation and kernels; the

@@ -43,16 +43,22 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t str
 // get zeros; with no destination the combination is kept alive in a
 // register so the loads still happen.  NR > 0 fixes both counts at compile
 // time (the 8-rank fused kernel's fully unrolled form); NR == 0 reads them.
+// TL adds a timeline: block b writes the device's constant-rate real-time
+// counter at its start to ts[2b], and after all of its stores have completed
+// to ts[2b + 1] (launched with at least one destination).
 struct StreamArgs {
     RankTable src;
     RankTable dst;
     size_t units;   // 16-byte units per buffer
     int nsrc;
     int ndst;
+    unsigned long long* ts;   // TL only
 };
 
-template <int NR, class CFG>
+template <int NR, class CFG, bool TL = false>
 __global__ __launch_bounds__(kFusedThreads) void k_stream(const StreamArgs a) {
+    unsigned long long t0 = 0;
+    if constexpr (TL) t0 = __builtin_amdgcn_s_memrealtime();
     constexpr int U = CFG::U;
     constexpr int kB = CFG::B;
     constexpr int kMax = NR > 0 ? NR : AR_MAX_RANKS;
@@ -108,6 +114,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_stream(const StreamArgs a) {
         for (int u = 0; u < U; ++u)
             if (ok[u]) st16<kFusedNT>(d + off[u], acc[u]);
     }
+    if constexpr (TL) {
+        __builtin_amdgcn_s_waitcnt(0);   // every load and store of the wave done
+        const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+        if (threadIdx.x == 0) {
+            a.ts[2 * (size_t)blockIdx.x] = t0;
+            a.ts[2 * (size_t)blockIdx.x + 1] = t1;
+        }
+    }
 }
 
 hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
@@ -122,6 +136,7 @@ hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int
     a.units = bytes / 16;
     a.nsrc = nsrc;
     a.ndst = ndst;
+    a.ts = nullptr;
     if (a.units == 0 || nsrc + ndst == 0) return hipSuccess;
     // the fused kernel's choice for an AllReduce of nsrc ranks of `bytes`
     // each: PACED (one unit per lane, capped) from 8 sources up when the
@@ -141,6 +156,25 @@ hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int
         hipLaunchKernelGGL((k_stream<8, FusedWide>), grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL((k_stream<0, FusedWide>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_timeline(void* const* bufs, int n, size_t bytes, unsigned lds,
+                                  unsigned long long* ts, hipStream_t stream) {
+    if (n < 1 || n > AR_MAX_RANKS || !ts) return hipErrorInvalidValue;
+    StreamArgs a;
+    for (int r = 0; r < AR_MAX_RANKS; ++r) a.src.p[r] = a.dst.p[r] = r < n ? bufs[r] : nullptr;
+    a.units = bytes / 16;
+    a.nsrc = a.ndst = n;
+    a.ts = ts;
+    if (a.units == 0) return hipSuccess;
+    const size_t blocks = ceil_div(a.units, (size_t)kFusedThreads * FusedPaced::U);
+    if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks), block(kFusedThreads);
+    if (n == 8)
+        hipLaunchKernelGGL((k_stream<8, FusedPaced, true>), grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL((k_stream<0, FusedPaced, true>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 

@@ -89,6 +89,13 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t str
 hipError_t launch_stream(const void* const* src, int nsrc, void* const* dst, int ndst,
                          size_t bytes, bool caps, hipStream_t stream);
 
+// The same stream in place over n buffers (each read, then written), in the
+// PACED shape with `lds` bytes of dynamic LDS per block, recording block b's
+// start and end on the device's real-time counter in ts[2b] and ts[2b + 1]
+// (ts holds 2 * ceil(bytes / 1024) entries).
+hipError_t launch_stream_timeline(void* const* bufs, int n, size_t bytes, unsigned lds,
+                                  unsigned long long* ts, hipStream_t stream);
+
 // On-device result checker (check.hip): pass 1 writes one partial record per
 // block (at most kCheckMaxBlocks) to `part`, pass 2 folds them into `out`.
 constexpr int kCheckThreads = 256;

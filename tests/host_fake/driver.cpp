@@ -774,6 +774,54 @@ int main() {
                   ncu == 0, "probe on the fake device");
         CHECK(fake_counters().device_allocs - allocs == 1 && fake_counters().device_frees - frees == 1,
               "probe tables not freed");
+        // the stream timeline: argument checks, one launch when they pass
+        {
+            void* tb[8];
+            for (int r = 0; r < 8; ++r) tb[r] = rank_addr(r, 0);
+            auto* ts = reinterpret_cast<unsigned long long*>(kAux);
+            const size_t bytes = (size_t)25 << 20, nblk = bytes / 1024;
+            size_t blocks = 0;
+            unsigned khz = 0;
+            const long launches = fake_counters().kernel_launches;
+            CHECK(ar_stream_timeline(nullptr, tb, 8, bytes, 0, ts, 2 * nblk, &blocks, &khz) ==
+                      AR_ERR_INVALID_ARG, "timeline NULL ctx");
+            CHECK(ar_stream_timeline(ctx, nullptr, 8, bytes, 0, ts, 2 * nblk, &blocks, &khz) ==
+                      AR_ERR_INVALID_ARG, "timeline NULL bufs");
+            CHECK(ar_stream_timeline(ctx, tb, 0, bytes, 0, ts, 2 * nblk, &blocks, &khz) ==
+                      AR_ERR_INVALID_ARG, "timeline 0 buffers");
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes + 8, 0, ts, 2 * nblk + 2, &blocks, &khz) ==
+                      AR_ERR_INVALID_ARG, "timeline bytes not a multiple of 16");
+            CHECK(ar_stream_timeline(ctx, tb, 8, 0, 0, ts, 2 * nblk, &blocks, &khz) ==
+                      AR_ERR_INVALID_ARG, "timeline 0 bytes");
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes, (64u << 10) + 1, ts, 2 * nblk, &blocks,
+                                     &khz) == AR_ERR_INVALID_ARG, "timeline LDS above 64 KiB");
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes, 0, ts, 2 * nblk - 1, &blocks, &khz) ==
+                      AR_ERR_INVALID_ARG, "timeline ts too short");
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes, 0, ts, 2 * nblk, &blocks, &khz) ==
+                      AR_OK, "timeline");
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes, 0,
+                                     reinterpret_cast<unsigned long long*>(kAux + 4), 2 * nblk,
+                                     &blocks, &khz) == AR_ERR_INVALID_ARG, "timeline ts misaligned");
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes, 0,
+                                     reinterpret_cast<unsigned long long*>(rank_addr(3, 4096)),
+                                     2 * nblk, &blocks, &khz) == AR_ERR_INVALID_ARG,
+                  "timeline ts overlapping a buffer");
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes, 0,
+                                     reinterpret_cast<unsigned long long*>(kBase - kStride), 2 * nblk,
+                                     &blocks, &khz) == AR_ERR_INVALID_ARG, "timeline ts on device 1");
+            void* mis[2] = {tb[0], rank_addr(1, 8)};
+            CHECK(ar_stream_timeline(ctx, mis, 2, bytes, 0, ts, 2 * nblk, &blocks, &khz) ==
+                      AR_ERR_INVALID_ARG, "timeline buffer not 16-byte aligned");
+            blocks = 0;
+            khz = 0;
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes - 16, 29696, ts, 2 * nblk, &blocks, &khz) ==
+                      AR_OK && blocks == nblk && khz == 100000, "timeline blocks %zu, clock %u kHz",
+                  blocks, khz);
+            CHECK(ar_stream_timeline(ctx, tb, 8, bytes, 0, ts, 2 * nblk, nullptr, nullptr) == AR_OK,
+                  "timeline without outputs");
+            CHECK(fake_counters().kernel_launches - launches == 3, "timeline launches: %ld",
+                  fake_counters().kernel_launches - launches);
+        }
         // leave a few graphs recorded: ar_destroy must release them
         CHECK(ar_set_graphs(ctx, SIZE_MAX) == AR_OK, "graphs on");
         void* bufs[kMaxN];

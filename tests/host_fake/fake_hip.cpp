@@ -194,6 +194,11 @@ hipError_t launch_stream(const void* const*, int, void* const*, int, size_t, boo
     ++g_count.kernel_launches;
     return hipSuccess;
 }
+hipError_t launch_stream_timeline(void* const*, int, size_t, unsigned, unsigned long long*,
+                                  hipStream_t) {
+    ++g_count.kernel_launches;
+    return hipSuccess;
+}
 unsigned check_blocks(size_t count) {
     const size_t want = (count + kCheckThreads - 1) / kCheckThreads;
     return (unsigned)(want == 0 ? 1 : want < kCheckMaxBlocks ? want : kCheckMaxBlocks);
@@ -219,6 +224,10 @@ hipError_t hipGetDeviceCount(int* count) {
 }
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
     if (device != 0) return set(hipErrorInvalidDevice);
+    if (attr == hipDeviceAttributeWallClockRate) {
+        *value = 100000;   // a 100 MHz clock
+        return hipSuccess;
+    }
     if (attr != hipDeviceAttributeMaxSharedMemoryPerMultiprocessor) return set(hipErrorInvalidValue);
     *value = g_lds_per_cu;
     return hipSuccess;
