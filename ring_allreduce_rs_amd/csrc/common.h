@@ -100,6 +100,15 @@ struct Unit<Op, true, NT> {
     __device__ static T ld(const char* p) { return ld16<NT>(p); }
     __device__ static void st(char* p, T v) { st16<NT>(p, v); }
     __device__ static T comb(T a, T b) { return comb4<Op>(a, b); }
+    // in-register folds: fold hop by hop, then canon once (LazyFold)
+    __device__ static T fold(T a, T b) {
+        if constexpr (LazyFold<Op>::value) return fold4<Op>(a, b);
+        else return comb4<Op>(a, b);
+    }
+    __device__ static T canon(T a) {
+        if constexpr (LazyFold<Op>::value) return canon4<Op>(a);
+        else return a;
+    }
     __device__ static T fin(T a, float nf, float inv) { return finish4<Op>(a, nf, inv); }
     __device__ static T zero() { return u32x4{0u, 0u, 0u, 0u}; }
 };
@@ -111,6 +120,15 @@ struct Unit<Op, false, NT> {
     __device__ static T ld(const char* p) { return ld_elem<Op::kElemBytes>(p); }
     __device__ static void st(char* p, T v) { st_elem<Op::kElemBytes>(p, v); }
     __device__ static T comb(T a, T b) { return Op::comb_elem(a, b); }
+    // (LazyFold ops have 4-byte elements: an element is a word)
+    __device__ static T fold(T a, T b) {
+        if constexpr (LazyFold<Op>::value) return Op::fold_word(a, b);
+        else return Op::comb_elem(a, b);
+    }
+    __device__ static T canon(T a) {
+        if constexpr (LazyFold<Op>::value) return Op::canon_word(a);
+        else return a;
+    }
     __device__ static T fin(T a, float nf, float inv) { return Op::finish_elem(a, nf, inv); }
     __device__ static T zero() { return 0u; }
 };

@@ -89,11 +89,11 @@ unsigned fused_waves_per_cu(const Plan& p) {
     }
     if (p.kind != KIND_FUSED_AR && p.kind != KIND_FUSED_RS) return 0;
     // How many waves a CU needs depends on the bytes a wave keeps in flight
-    // and on the fold's ALU work per byte: the IEEE maximum of fp32 / bf16
-    // (NaN handling, bf16 widening) wants more waves than an add or an
-    // integer max.  Each cap is the best of a sweep over 3-16 waves per CU
-    // (or none), measured on MI355X with cold inputs (fp32 unless named):
-    const bool fmax = p.op == AR_MAX && p.dtype != AR_INT32;
+    // and on the fold's ALU work per byte: bf16 (widening, rounding, and for
+    // MAX the NaN rules hop by hop) wants more waves than an add, an integer
+    // max or fp32 MAX (one hardware maximum per hop).  Each cap is the best
+    // of a sweep over 3-16 waves per CU (or none), measured on MI355X with
+    // cold inputs (fp32 unless named):
     if (cfg == CFG_PACED) {
         // ReduceScatter (N reads, one write): 8 x 25 MiB 39.8 -> 38.6 us,
         // 16 x 256 MiB int32 787 -> 720 us
@@ -105,12 +105,11 @@ unsigned fused_waves_per_cu(const Plan& p) {
         // 8 x 128 Mi elements 693 us at 6-7, 8 x 12.5 Mi AVG 68.9 us at 6
         // (71.0 at 5)
         if (p.dtype == AR_BFLOAT16) return 6;
-        // fp32 MAX: 8 x 25 MiB 68.0 us at 6 (69.5 at 7, 71.8 at 5), 16 x 1 GiB
-        // 5.63 ms at 6 (6.69 at 4)
-        if (fmax) return 6;
-        // ring and double-tree SUM / AVG, int32 MAX: 8 x 25 MiB 69.7 us at 5
+        // ring and double-tree SUM / AVG / MAX: 8 x 25 MiB 69.7 us at 5
         // (70.7 at 4 and 6), 12 x 64 MiB 261 us at 5, 16 x 64 MiB 342 us at
-        // 4-5, 16 x 1 GiB int32 MAX 5.68 ms at 5 (6.20 uncapped).  (How the
+        // 4-5, 16 x 1 GiB int32 MAX 5.68 ms at 5 (6.20 uncapped), fp32 MAX
+        // 8 x 25 MiB 70.1 us at 5 (71.4 at 6), 16 x 268,435,459 5.72 ms at
+        // 5 (5.77 at 6).  (How the
         // rank buffers sit in HBM moves the best cap by one: with
         // back-to-back buffers 8 x 25 MiB ran 67.8 us at 4 and 68.9 at 5.)
         return kPacedRingWaves;
@@ -130,12 +129,10 @@ unsigned fused_waves_per_cu(const Plan& p) {
             return p.nranks > 16 ? 4 : 7;
         }
         if (p.nranks <= 16) return 0;
-        // fp32 MAX: 64 x 16 MiB 459 -> 421 us (5; 515 at 3), 32 x 32 MiB
-        // 413 -> 378 us (5; 455 at 3)
-        if (fmax) return 5;
-        // fp32 SUM / AVG, int32 SUM / MAX: 64 x 8 MiB 230.5 -> 202.5 us,
-        // 64 x 64 MiB 1572 -> 1490 us, 32 x 32 MiB 403 -> 350 us, 64 x 16 MiB
-        // int32 MAX 464 -> 383 us (all at 3)
+        // fp32 / int32: 64 x 8 MiB 230.5 -> 202.5 us, 64 x 64 MiB 1572 ->
+        // 1490 us, 32 x 32 MiB 403 -> 350 us, 64 x 16 MiB int32 MAX 464 ->
+        // 383 us, fp32 MAX 476 -> 394 us, 32 x 32 MiB fp32 MAX 407 -> 354
+        // us (all at 3)
         return 3;
     }
     if (cfg == CFG_DEEP && p.kind == KIND_FUSED_RS) {
@@ -151,12 +148,12 @@ unsigned fused_waves_per_cu(const Plan& p) {
             // (8; 198 at 6, 179 at 10)
             return p.op == AR_MAX ? 0 : 8;
         }
-        // fp32 MAX: 64 x 16 MiB 194.6 -> 188.5 us (8; 187.0 at 10, 217.8 at
-        // 6); fp32 SUM / AVG, int32 SUM / MAX at 5: 64 x 16 MiB 191.7 ->
-        // 172.3 us, 64 x 8 MiB 98.2 -> 91.5, 32 x 32 MiB 179.5 -> 167.9,
-        // 32 x 32 MiB int32 MAX 181.5 -> 168.9, 64 x 64 MiB 684.5 -> 656.4
-        // (4 and 6 within 1-3 % of 5, 3 and 10 worse)
-        return fmax ? 8 : 5;
+        // fp32 / int32 at 5: 64 x 16 MiB 191.7 -> 172.3 us, 64 x 8 MiB 98.2
+        // -> 91.5, 32 x 32 MiB 179.5 -> 167.9, 32 x 32 MiB int32 MAX 181.5 ->
+        // 168.9, 64 x 64 MiB 684.5 -> 656.4, fp32 MAX 64 x 16 MiB 190.5 ->
+        // 172.8, 32 x 32 MiB 180.0 -> 167.8 (4 and 6 within 1-3 % of 5, 3,
+        // 8 and 10 worse)
+        return 5;
     }
     return 0;
 }

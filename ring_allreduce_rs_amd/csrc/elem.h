@@ -18,6 +18,8 @@
 // int32 lanes or 8 bf16 lanes.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -114,6 +116,18 @@ struct OpF32Max {
     __device__ static uint32_t finish_elem(uint32_t a, float, float) { return a; }
     __device__ static uint32_t comb_word(uint32_t a, uint32_t b) { return fmaximum_bits(a, b); }
     __device__ static uint32_t finish_word(uint32_t a, float, float) { return a; }
+    // A fold kept in registers takes the hardware's IEEE-754-2019 maximum (a
+    // NaN if either operand is one, -0 below +0; gfx950 issues it as
+    // v_maximum3_f32, two hops per instruction) and makes a NaN canonical
+    // once, at the end.  A maximum is one of its operands and does not depend
+    // on the order of the fold, so the bits are those of the rule above
+    // applied hop by hop.
+    __device__ static uint32_t fold_word(uint32_t a, uint32_t b) {
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(as_f32(a), as_f32(b)));
+    }
+    __device__ static uint32_t canon_word(uint32_t a) {
+        return as_f32(a) != as_f32(a) ? 0x7fc00000u : a;
+    }
 };
 
 struct OpBF16Sum {
@@ -189,6 +203,33 @@ __device__ __forceinline__ u32x4 comb4(u32x4 a, u32x4 b) {
     r.y = Op::comb_word(a.y, b.y);
     r.z = Op::comb_word(a.z, b.z);
     r.w = Op::comb_word(a.w, b.w);
+    return r;
+}
+
+// Ops with a fold_word: an in-register fold uses it and ends with canon_word
+// (see OpF32Max); the others fold with comb_word.
+template <class Op, class = void>
+struct LazyFold : std::false_type {};
+template <class Op>
+struct LazyFold<Op, std::void_t<decltype(&Op::fold_word)>> : std::true_type {};
+
+template <class Op>
+__device__ __forceinline__ u32x4 fold4(u32x4 a, u32x4 b) {
+    u32x4 r;
+    r.x = Op::fold_word(a.x, b.x);
+    r.y = Op::fold_word(a.y, b.y);
+    r.z = Op::fold_word(a.z, b.z);
+    r.w = Op::fold_word(a.w, b.w);
+    return r;
+}
+
+template <class Op>
+__device__ __forceinline__ u32x4 canon4(u32x4 a) {
+    u32x4 r;
+    r.x = Op::canon_word(a.x);
+    r.y = Op::canon_word(a.y);
+    r.z = Op::canon_word(a.z);
+    r.w = Op::canon_word(a.w);
     return r;
 }
 

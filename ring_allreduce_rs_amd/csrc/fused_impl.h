@@ -31,6 +31,24 @@ namespace arlib {
 // arguments.
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
+// A pause (s_sleep, in units of 64 cycles) between the fold and the stores
+// of the 8-rank PACED ring and double-tree AllReduce over fp32.  Measured on
+// MI355X in one process, pause 16 against none: 8 x 25 MiB AVG 69.9 -> 68.6
+// us and 72.7 -> 71.8 us (two boxes), SUM 72.7 -> 71.8, MAX 70.0 -> 69.1,
+// double tree 69.9 -> 68.8; 8 x 100-200 MiB 2.4-2.9 % faster.  The int32
+// kernels re-read their rank pointers from the argument block between the
+// fold and the stores, which already delays their stores by a scalar
+// round trip: a pause slowed them (8 x 25 MiB SUM 68.9 -> 71.7 us), as it
+// did bf16 (71.5 -> 74.6), the pairwise orders (72.8 -> 73.9) and left the
+// run-time rank count and the ReduceScatter level.
+template <class Op, int MODE, int NR, class CFG, int ORDER>
+constexpr int kStorePause =
+    (std::is_same_v<CFG, FusedPaced> && NR == 8 && MODE == KIND_FUSED_AR &&
+     (ORDER == ORDER_RING || ORDER == ORDER_DTREE) &&
+     (std::is_same_v<Op, OpF32Sum> || std::is_same_v<Op, OpF32Max>))
+        ? 16
+        : 0;
+
 template <class Op, int MODE, bool VEC, int NR, class CFG, int ORDER = ORDER_RING,
           bool LEAD = false>
 __device__ __forceinline__ void fused_units(const Args& a, int c, int start, size_t byte0,
@@ -101,7 +119,7 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
                 for (int j = 0; j + w < kB; j += 2 * w) {
                     if (j + w < bn) {
 #pragma unroll
-                        for (int u = 0; u < U; ++u) v[j][u] = X::comb(v[j][u], v[j + w][u]);
+                        for (int u = 0; u < U; ++u) v[j][u] = X::fold(v[j][u], v[j + w][u]);
                     }
                 }
             }
@@ -111,7 +129,7 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
             for (int l = 0; l < kLevels; ++l) {
                 if ((k >> l) & 1) {
 #pragma unroll
-                    for (int u = 0; u < U; ++u) acc[u] = X::comb(st[l][u], acc[u]);
+                    for (int u = 0; u < U; ++u) acc[u] = X::fold(st[l][u], acc[u]);
                 } else {
 #pragma unroll
                     for (int u = 0; u < U; ++u) st[l][u] = acc[u];
@@ -174,18 +192,18 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
                         const int m = (2 << i) - 2;
                         if ((p & m) == m) {
 #pragma unroll
-                            for (int u = 0; u < U; ++u) cur[u] = X::comb(pend[i][u], cur[u]);
+                            for (int u = 0; u < U; ++u) cur[u] = X::fold(pend[i][u], cur[u]);
                         }
                     }
                 } else {
                     const int lvl = __builtin_ctz((unsigned)p);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) pend[lvl][u] = X::comb(cur[u], v[j][u]);
+                    for (int u = 0; u < U; ++u) pend[lvl][u] = X::fold(cur[u], v[j][u]);
                 }
             }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = n > 1 ? X::comb(root[u], cur[u]) : root[u];
+        for (int u = 0; u < U; ++u) acc[u] = n > 1 ? X::fold(root[u], cur[u]) : root[u];
     }
     if constexpr (MODE != KIND_FUSED_AG) {
         if constexpr (ORDER == ORDER_RING) {
@@ -222,15 +240,25 @@ __device__ __forceinline__ void fused_units(const Args& a, int c, int start, siz
                 if (j0 + j < n) {
 #pragma unroll
                     for (int u = 0; u < U; ++u)
-                        acc[u] = (j0 + j == 0) ? v[j][u] : X::comb(acc[u], v[j][u]);
+                        acc[u] = (j0 + j == 0) ? v[j][u] : X::fold(acc[u], v[j][u]);
                 }
             }
             r = rr;
         }
         }  // ORDER_RING
+        // every order folds with X::fold; a NaN becomes canonical here
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = X::canon(acc[u]);
         if (a.avg) {
 #pragma unroll
             for (int u = 0; u < U; ++u) acc[u] = X::fin(acc[u], a.nf, a.inv);
+        }
+        if constexpr (kStorePause<Op, MODE, NR, CFG, ORDER> > 0) {
+            // the empty asm needs the folded values, so the fold (and any
+            // AVG division) finishes before the pause begins
+#pragma unroll
+            for (int u = 0; u < U; ++u) asm volatile("" ::"v"(acc[u]));
+            __builtin_amdgcn_s_sleep(kStorePause<Op, MODE, NR, CFG, ORDER>);
         }
         if constexpr (MODE == KIND_FUSED_RS) {
             char* dst = rank_ptr(a, c);

@@ -708,11 +708,10 @@ void check_residency_caps() {
                                 // the ReduceScatter's DEEP caps: beyond 16 ranks and
                                 // 256 MiB, bf16 MAX excepted
                                 if (cfg == CFG_DEEP && kind == KIND_FUSED_RS) {
-                                    const bool fmax = op == AR_MAX && dt != AR_INT32;
                                     const unsigned want =
                                         total <= kDeepCapMinBytes || n <= 16 ? 0u
                                         : dt == AR_BFLOAT16 ? (op == AR_MAX ? 0u : 8u)
-                                                            : (fmax ? 8u : 5u);
+                                                            : 5u;
                                     CHECK(w == want, "ReduceScatter DEEP cap %u (want %u) n=%d dt=%d op=%d",
                                           w, want, n, dt, op);
                                 }
