@@ -1,7 +1,8 @@
 """fp32 MAX over special values, every fused shape against the oracle.
 
-The one-pass ring folds fp32 MAX in registers with the hardware's IEEE-754-2019
-maximum and makes a NaN canonical once, at the end; the rule the pages' max
+The one-pass kernels (every fold order) take fp32 MAX in registers with the
+hardware's IEEE-754-2019 maximum and make a NaN canonical once, at the end; the
+rule the pages' max
 reduction is given here (NaN if any operand is NaN, canonical 0x7FC00000; -0
 below +0) is applied hop by hop by the per-step kernels and by the oracle.
 These inputs mix NaNs of every sign and payload (quiet and signalling),
