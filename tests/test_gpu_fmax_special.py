@@ -1,10 +1,10 @@
 """fp32 MAX over special values, every fused shape against the oracle.
 
 The one-pass kernels (every fold order) take fp32 MAX in registers with the
-hardware's IEEE-754-2019 maximum and make a NaN canonical once, at the end; the
-rule the pages' max
-reduction is given here (NaN if any operand is NaN, canonical 0x7FC00000; -0
-below +0) is applied hop by hop by the per-step kernels and by the oracle.
+hardware's IEEE-754-2019 maximum and make a NaN canonical once, at the end.
+The rule given to the pages' max reduction here (NaN if any operand is NaN,
+canonical 0x7FC00000; -0 below +0) is applied hop by hop by the per-step
+kernels and by the oracle.
 These inputs mix NaNs of every sign and payload (quiet and signalling),
 signed zeros, infinities, subnormals and normal values, across the 8-rank
 compiled loop, the run-time rank count, the DEEP and TINY shapes, the PACED
