@@ -200,7 +200,7 @@ double predict_allreduce_us(int algo, int n, size_t count, size_t eb) {
 // The argmin over every algorithm; ties keep the earlier candidate.  The
 // one-pass forms share one prediction (one launch, 2NK bytes), so the fused
 // ring, listed first, takes every tie: on MI355X the one-pass tree orders
-// measured within 3 % of it either way, less than the spread between boxes.
+// measured within 3 % of it either way, less than the spread between machines.
 int auto_algo(int n, size_t count, size_t eb) {
     int best = AR_ALGO_RING_FUSED;
     double best_us = predict_allreduce_us(best, n, count, eb);

@@ -34,7 +34,7 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 // A pause (s_sleep, in units of 64 cycles) between the fold and the stores
 // of the 8-rank PACED ring and double-tree AllReduce over fp32.  Measured on
 // MI355X in one process, pause 16 against none: 8 x 25 MiB AVG 69.9 -> 68.6
-// us and 72.7 -> 71.8 us (two boxes), SUM 72.7 -> 71.8, MAX 70.0 -> 69.1,
+// us and 72.7 -> 71.8 us (two machines), SUM 72.7 -> 71.8, MAX 70.0 -> 69.1,
 // double tree 69.9 -> 68.8; 8 x 100-200 MiB 2.4-2.9 % faster.  The int32
 // kernels re-read their rank pointers from the argument block between the
 // fold and the stores, which already delays their stores by a scalar
