@@ -96,3 +96,50 @@ def test_captured_capped_allreduce_replays_match_oracle(dtype, op, count):
         assert ar.check(ts)["mismatched"] == 0
     del src, ts, g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("coll", ["allgather", "reduce_scatter"])
+def test_captured_capped_allgather_and_reduce_scatter_replay(coll):
+    """The AllGather and ReduceScatter just above 128 MiB run their own capped
+    PACED kernels (14 and 10 waves per CU); captured by the caller, every
+    replay matches the oracle."""
+    n, count, dtype = 8, (4 << 20) + 3, "float32"
+    rng = np.random.Generator(np.random.PCG64(count + len(coll)))
+    inputs = [[rng.standard_normal(count, dtype=np.float32) for _ in range(n)] for _ in range(3)]
+    src = [to_gpu(xs, dtype) for xs in inputs]
+    ts = [torch.empty_like(t) for t in src[0]]
+
+    def call():
+        if coll == "allgather":
+            ar.allgather(ts, algo="ring_fused")
+        else:
+            ar.reduce_scatter(ts, op="sum", algo="ring_fused")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for t, s in zip(ts, src[0]):
+            t.copy_(s)
+        call()                                          # warm-up on the capture stream
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            call()
+    torch.cuda.synchronize()
+    for rep, xs in enumerate(inputs):
+        for t, s in zip(ts, src[rep]):                  # eager work between replays
+            t.copy_(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if coll == "allgather":
+            want = oracle.simulate_ring_allgather(xs, dtype).state
+            for r in (0, 3, n - 1):
+                assert_bits_equal(to_np(ts[r]), want[r], f"AllGather replay {rep} rank {r}")
+        else:
+            want = oracle.ordered_ring_fold(xs, dtype, "sum")
+            for r, (lo, ln) in enumerate(oracle.chunk_layout(count, n)):
+                assert_bits_equal(to_np(ts[r][lo:lo + ln]), want[lo:lo + ln],
+                                  f"ReduceScatter replay {rep} owner {r}")
+    del src, ts, g
+    torch.cuda.empty_cache()
