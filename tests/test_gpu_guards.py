@@ -5,7 +5,9 @@ trailing guard regions hold a sentinel bit pattern; after each collective the
 guards must be bit-for-bit unchanged and the views must hold the oracle's
 result.  Counts cover ragged chunks, counts below N and empty chunks, and the
 views start at several element offsets from a 16-byte boundary, so the
-element-wise head and tail paths run next to the guards."""
+element-wise head and tail paths run next to the guards.  The residency-capped
+shapes of the AllReduce, AllGather and ReduceScatter run at the sizes that
+select them."""
 
 import numpy as np
 import pytest
@@ -108,3 +110,42 @@ def test_reduce_scatter_and_allgather_write_only_their_buffers(algo, n, count):
         want = AR_SIMS[algo](xs, dtype, op).state
         for r in range(n):
             assert_bits_equal(to_np(views[r]), want[r], f"RS+AG {algo} n={n} rank {r}")
+
+
+# The residency-capped shapes (calls above 128 MiB; the AllGather beyond 8
+# ranks above 512 MiB; the ReduceScatter's capped DEEP shape beyond 16 ranks
+# above 256 MiB), next to guards, with chunk bodies on and off 16-byte units
+BIG = [("allreduce", 8, "float32", (4 << 20) + 3, 0), ("allreduce", 8, "float32", (4 << 20) + 3, 3),
+       ("allreduce", 16, "int32", (2 << 20) + 5, 1), ("allgather", 8, "float32", (4 << 20) + 3, 2),
+       ("allgather", 16, "int32", (8 << 20) + 5, 0), ("reduce_scatter", 8, "float32", (4 << 20) + 3, 1),
+       ("reduce_scatter", 32, "int32", (2 << 20) + 7, 2)]
+
+
+@pytest.mark.parametrize("coll,n,dtype,count,shift", BIG,
+                         ids=[f"{c[0]}-n{c[1]}-{c[2]}-s{c[4]}" for c in BIG])
+def test_capped_kernels_write_only_their_buffers(coll, n, dtype, count, shift):
+    xs = _inputs(dtype, n, count, seed=n * 1000 + count + shift)
+    fulls, views = _guarded(xs, dtype, shift)
+    op = "avg" if dtype == "float32" and coll == "allreduce" else "sum"
+    if coll == "allreduce":
+        ar.allreduce(views, op=op, algo="ring_fused")
+    elif coll == "allgather":
+        ar.allgather(views, algo="ring_fused")
+    else:
+        ar.reduce_scatter(views, op=op, algo="ring_fused")
+    torch.cuda.synchronize()
+    _check_guards(fulls, dtype, shift, count, f"{coll} n={n} shift={shift}")
+    if coll == "allgather":
+        want = oracle.simulate_ring_allgather(xs, dtype).state
+        for r in (0, n - 1):
+            assert_bits_equal(to_np(views[r]), want[r], f"AllGather rank {r}")
+    else:
+        want = oracle.ordered_ring_fold(xs, dtype, op)
+        if coll == "allreduce":
+            for r in (0, n - 1):
+                assert_bits_equal(to_np(views[r]), want, f"AllReduce rank {r}")
+        else:
+            for r, (lo, ln) in enumerate(oracle.chunk_layout(count, n)):
+                assert_bits_equal(to_np(views[r][lo:lo + ln]), want[lo:lo + ln], f"RS owner {r}")
+    del fulls, views
+    torch.cuda.empty_cache()
