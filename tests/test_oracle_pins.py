@@ -609,3 +609,27 @@ def test_dtree_traffic_closed_form(n):
         assert tr.sent[r] == want == tr.recv[r]
     with pytest.raises(oracle.BrokenRing):
         oracle.simulate_double_tree_allreduce(xs, "float32", "sum", drop=(1, 0))
+
+
+def test_sampled_tree_folds_equal_the_whole_vector_folds():
+    """The per-position forms that the full-size GPU tests call on sampled
+    columns (tree_fold_at, dtree_fold_at, ring_fold_at) give, column by
+    column, the whole-vector folds that the goldens above pin."""
+    rng = np.random.Generator(np.random.PCG64(404))
+    for n in (2, 4, 8, 16):
+        count = 6 * n + 5
+        xs = [rng.standard_normal(count).astype(np.float32) for _ in range(n)]
+        vals = np.stack(xs)
+        cols = np.array([0, 1, count // 2, count - 1])
+        for op in ("sum", "max", "avg"):
+            tree = oracle.pairwise_tree_fold(xs, "float32", op)
+            assert (_bits(oracle.tree_fold_at(vals[:, cols], "float32", op)) == _bits(tree[cols])).all()
+            dt = oracle.double_tree_fold(xs, "float32", op)
+            ring = oracle.ordered_ring_fold(xs, "float32", op)
+            chunk = np.array([oracle.chunk_of(int(i), count, n) for i in cols])
+            assert (_bits(oracle.ring_fold_at(vals[:, cols], chunk, n, "float32", op))
+                    == _bits(ring[cols])).all()
+            first = (count + 1) // 2
+            for tree_id, sel in ((0, cols[cols < first]), (1, cols[cols >= first])):
+                got = oracle.dtree_fold_at(vals[:, sel], tree_id, "float32", op)
+                assert (_bits(got) == _bits(dt[sel])).all(), (n, op, tree_id)
